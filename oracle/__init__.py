@@ -1,0 +1,37 @@
+"""CPU oracle for lazy-RoPE paged attention -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import anything from this package.  The product path (the HIP library and its
+Python binding) never imports, links or executes it, and shares no code with
+it: the oracle recomputes RoPE frequencies, rotations and softmax attention
+itself, in float64, from the definitions in "LazyAttention: Efficient
+Retrieval-Augmented Generation with Deferred Positional Encoding" (§3.1
+Eq. 4 and the RoPE form of attention, §3.2 Fact 3.2 and the rotation
+formula, §2 Eqs. 1-3, §3.1-§3.2 cost model).
+
+Pinned by tests/test_oracle.py (see each function's docstring for its pin).
+Parity unpinned: none of the pages print attention outputs, so beyond the
+invariants, special cases and brute force listed there, the oracle's outputs
+rest on the definition of RoPE attention itself.
+"""
+from .lazy_oracle import (  # noqa: F401
+    rope_theta,
+    rope_rotate,
+    gather_request,
+    attention_decode,
+    attention_prefill,
+    attention_decode_relative,
+    run_decode,
+    run_prefill,
+)
+from .analysis import (  # noqa: F401
+    hit_ratio_agnostic,
+    hit_ratio_aware,
+    hit_ratio_gap,
+    naive_flops_overhead,
+    naive_io_overhead,
+    prefill_flops_overhead,
+    prefill_table_bandwidth,
+    decode_trigger_overhead,
+    decode_overhead,
+)

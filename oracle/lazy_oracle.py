@@ -1,0 +1,236 @@
+"""Plain float64 oracle of attention over a position-free paged KV pool.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and
+bench.py's cpu_baseline leg, never by the product path.
+
+What it computes.  LazyAttention (§1, §3.1 "Deferred encoding") stores keys
+and values without positions and claims results identical to eagerly
+re-encoding the cache at each request's positions.  The oracle therefore
+computes the plain definition: it *materialises* the re-encoded keys
+R_p k for every key at its logical position p, rotates the query to its own
+position, and runs textbook softmax attention (§3.1 Eq. 4 with RoPE applied to
+Q and K).  Nothing is tiled, fused or reordered.
+
+Readings of the pages (listed with reasons in the design notes):
+  * RoPE pairs dimension i with i + D/2 (the "half-dimension" K1/K2 split of
+    §3.2 "Prefilling" and the Fig. 3 caption), rotating by +p*theta_i as in
+    the §3.2 rotation formula k1' = k1 cos - k2 sin, k2' = k1 sin + k2 cos;
+  * theta_i = base^(-2i/D), i < D/2 (the frequencies are never printed; the
+    pages write the angle as m*theta_i in App. C.4);
+  * scale 1/sqrt(D) multiplies the rotated q.k (Eq. 4);
+  * GQA: query head h reads kv head floor(h / G) (§3.5 "GQA/MQA");
+  * decode attends exactly the listed segments; prefill sees every cached
+    key and, among the new tokens, keys at positions <= the query's.
+
+Inputs are the exact values handed to the GPU: bf16 pools/queries arrive as
+uint16 bit patterns and are widened exactly to float64 here.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rope_theta",
+    "rope_rotate",
+    "gather_request",
+    "attention_decode",
+    "attention_prefill",
+    "attention_decode_relative",
+    "run_decode",
+    "run_prefill",
+]
+
+
+def _as_f64(a) -> np.ndarray:
+    """Widen float or bf16-bit (uint16) arrays to float64 exactly."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def rope_theta(head_dim: int, base: float) -> np.ndarray:
+    """RoPE frequencies theta_i = base^(-2i/D), i = 0 .. D/2-1, in float64.
+
+    Pin: the identity table (theta = 0) special case and the textbook causal
+    RoPE attention special case in tests/test_oracle.py.
+    """
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * i / float(head_dim))
+
+
+def rope_rotate(x, pos, theta) -> np.ndarray:
+    """Rotate x[..., D] to position(s) pos (broadcast over leading axes).
+
+    Pair (i, i+D/2) is rotated by angle pos*theta_i:
+      y_i = x_i cos - x_{i+D/2} sin,   y_{i+D/2} = x_i sin + x_{i+D/2} cos
+    (§3.2 "Prefilling", the relative-rotation formula with the offset taken
+    as the absolute position).
+
+    Pins: equals multiplication of x_i + j x_{i+D/2} by exp(j pos theta_i)
+    (RoPE's complex form, computed with numpy complex arithmetic); Fact 3.2
+    (R_m q).(R_n k) = q.R_{n-m} k; norm preservation; rot(x, 0) = x.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.float64)
+    half = x.shape[-1] // 2
+    ang = pos[..., None] * np.asarray(theta, dtype=np.float64)
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def gather_request(k_pool, v_pool, segments, block_size: int, kv_head: int):
+    """Collect one request's keys/values for one kv head, in table order.
+
+    Token t of a segment starting at s lives in block blocks[t // BS], slot
+    t % BS, at logical position s + t.  Returns (K [n, D], V [n, D] float64,
+    positions [n] int64, is_new [n] bool).
+    """
+    ks, vs, ps, ns = [], [], [], []
+    for seg in segments:
+        n = int(seg.n_tokens)
+        if n == 0:
+            continue
+        t = np.arange(n)
+        blk = np.asarray(seg.blocks, dtype=np.int64)[t // block_size]
+        slot = t % block_size
+        ks.append(_as_f64(k_pool[blk, kv_head, slot, :]))
+        vs.append(_as_f64(v_pool[blk, kv_head, slot, :]))
+        ps.append(int(seg.start) + t)
+        ns.append(np.full(n, bool(seg.is_new)))
+    if not ks:
+        D = k_pool.shape[-1]
+        return (np.zeros((0, D)), np.zeros((0, D)), np.zeros(0, np.int64), np.zeros(0, bool))
+    return np.concatenate(ks), np.concatenate(vs), np.concatenate(ps), np.concatenate(ns)
+
+
+def _softmax_attend(scores: np.ndarray, V: np.ndarray):
+    """Textbook softmax over the last axis (Eq. 4), returning (out, lse)."""
+    if scores.shape[-1] == 0:
+        raise ValueError("attention over zero keys is undefined")
+    mx = np.max(scores, axis=-1, keepdims=True)
+    if not np.all(np.isfinite(mx)):
+        raise ValueError("a query row sees no key (fully masked)")
+    e = np.exp(scores - mx)
+    z = np.sum(e, axis=-1, keepdims=True)
+    out = (e @ V) / z
+    lse = (mx + np.log(z))[..., 0]
+    return out, lse
+
+
+def attention_decode(q, q_pos, segments, k_pool, v_pool, *, block_size, num_kv_heads,
+                     theta, scale, rotate=True):
+    """One decode query (all heads) of one request, eager RoPE.
+
+    q: [Hq, D]; q_pos: the query's logical position m.  Keys are gathered,
+    re-encoded at their positions (the materialised cache the method avoids)
+    and attended with textbook softmax.  Returns out [Hq, D], lse [Hq].
+    rotate=False drops RoPE entirely (used by the identity-table pin).
+    """
+    qf = _as_f64(q)
+    Hq, D = qf.shape
+    G = Hq // num_kv_heads
+    out = np.empty((Hq, D))
+    lse = np.empty(Hq)
+    for g in range(num_kv_heads):
+        K, V, pos, _ = gather_request(k_pool, v_pool, segments, block_size, g)
+        qs = qf[g * G:(g + 1) * G]
+        if rotate:
+            Kt = rope_rotate(K, pos, theta)
+            qt = rope_rotate(qs, np.full(G, q_pos), theta)
+        else:
+            Kt, qt = K, qs
+        s = scale * (qt @ Kt.T)
+        o, l = _softmax_attend(s, V)
+        out[g * G:(g + 1) * G] = o
+        lse[g * G:(g + 1) * G] = l
+    return out, lse
+
+
+def attention_decode_relative(q, q_pos, segments, k_pool, v_pool, *, block_size, num_kv_heads,
+                              theta, scale):
+    """Same decode query, computed the lazy way on the un-rotated pool.
+
+    Each score is scale * q^T R_{p-m} k (Fact 3.2, §3.2): only the relative
+    offset p - m is applied, to the stored key; the query stays un-rotated.
+    Pin: must equal attention_decode (eager) to 1e-12.
+    """
+    qf = _as_f64(q)
+    Hq, D = qf.shape
+    G = Hq // num_kv_heads
+    out = np.empty((Hq, D))
+    lse = np.empty(Hq)
+    for g in range(num_kv_heads):
+        K, V, pos, _ = gather_request(k_pool, v_pool, segments, block_size, g)
+        Kr = rope_rotate(K, pos - int(q_pos), theta)
+        s = scale * (qf[g * G:(g + 1) * G] @ Kr.T)
+        o, l = _softmax_attend(s, V)
+        out[g * G:(g + 1) * G] = o
+        lse[g * G:(g + 1) * G] = l
+    return out, lse
+
+
+def attention_prefill(q, q_pos0, segments, k_pool, v_pool, *, block_size, num_kv_heads,
+                      theta, scale, rotate=True, rows=None):
+    """New-token attention of one request, eager RoPE.
+
+    q: [T, Hq, D]; new token j sits at position q_pos0 + j.  Keys of cached
+    segments are all visible; keys of the new-token segment are visible iff
+    their position is <= the query's.  rows optionally restricts the query
+    rows computed (sampled parity).  Returns out [T', Hq, D], lse [T', Hq].
+    """
+    qf = _as_f64(q)
+    T, Hq, D = qf.shape
+    G = Hq // num_kv_heads
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    qpos = int(q_pos0) + rows
+    out = np.empty((len(rows), Hq, D))
+    lse = np.empty((len(rows), Hq))
+    for g in range(num_kv_heads):
+        K, V, pos, new = gather_request(k_pool, v_pool, segments, block_size, g)
+        Kt = rope_rotate(K, pos, theta) if rotate else K
+        visible = (~new)[None, :] | (pos[None, :] <= qpos[:, None])  # [T', n]
+        for hh in range(G):
+            h = g * G + hh
+            qs = qf[rows, h, :]
+            qt = rope_rotate(qs, qpos, theta) if rotate else qs
+            s = scale * (qt @ Kt.T)
+            s = np.where(visible, s, -np.inf)
+            o, l = _softmax_attend(s, V)
+            out[:, h, :] = o
+            lse[:, h] = l
+    return out, lse
+
+
+def _theta_of(w):
+    return rope_theta(w.head_dim, w.rope_base)
+
+
+def run_decode(w, requests=None, rotate=True):
+    """Oracle outputs for decode workload w: {r: (out [Hq, D], lse [Hq])}."""
+    th = _theta_of(w)
+    reqs = range(w.batch) if requests is None else requests
+    res = {}
+    for r in reqs:
+        res[r] = attention_decode(w.q[r], int(w.q_pos[r]), w.requests[r], w.k_pool, w.v_pool,
+                                  block_size=w.block_size, num_kv_heads=w.num_kv_heads,
+                                  theta=th, scale=w.scale, rotate=rotate)
+    return res
+
+
+def run_prefill(w, requests=None, rows=None, rotate=True):
+    """Oracle outputs for prefill workload w: {r: (out [T', Hq, D], lse [T', Hq])}.
+
+    rows, if given, maps request -> array of new-token indices to compute.
+    """
+    th = _theta_of(w)
+    reqs = range(w.batch) if requests is None else requests
+    res = {}
+    for r in reqs:
+        a, b = int(w.cu_q[r]), int(w.cu_q[r + 1])
+        rr = None if rows is None else rows.get(r)
+        res[r] = attention_prefill(w.q[a:b], int(w.q_pos[r]), w.requests[r], w.k_pool, w.v_pool,
+                                   block_size=w.block_size, num_kv_heads=w.num_kv_heads,
+                                   theta=th, scale=w.scale, rotate=rotate, rows=rr)
+    return res

@@ -1,0 +1,392 @@
+"""Pins of the CPU oracle against what the LazyAttention paper and mathematics fix.
+
+Every check here is independent of the oracle's own formulas: RoPE's complex
+form, torch's scaled_dot_product_attention (float64, CPU), scipy's Hurwitz
+zeta, closed forms of softmax, a pure-Python brute force, invariances the
+paper states (Fact 3.2 and the shift invariance it implies, zero-copy reuse),
+and the numbers the paper prints.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (
+    attention_decode,
+    attention_decode_relative,
+    attention_prefill,
+    decode_trigger_overhead,
+    hit_ratio_gap,
+    naive_flops_overhead,
+    naive_io_overhead,
+    prefill_flops_overhead,
+    prefill_table_bandwidth,
+    rope_rotate,
+    rope_theta,
+    run_decode,
+    run_prefill,
+)
+from oracle.analysis import zipf_partial_sum
+from oracle.brute import brute_attention
+from workloads import Segment, bf16_bits_to_f32, build_workload, make_config
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "paper_figures.json")
+RNG = np.random.default_rng(7)
+
+
+def _tiny(kind="decode", dtype="bf16", Hq=4, Hkv=2, D=16, BS=4, base=1e4, requests=None,
+          doc_lens=(7, 9, 4, 12), seed=3, poison=False):
+    if requests is None:
+        if kind == "decode":
+            requests = [[("doc", 0), ("doc", 1), ("priv", 3)],
+                        [("doc", 1), ("doc", 2), ("doc", 0, 40)],
+                        [("doc", 3), ("doc", 1), ("doc", 3, 100)]]
+        else:
+            requests = [[("doc", 0), ("doc", 2), ("new", 6)],
+                        [("doc", 3), ("doc", 0), ("new", 9)]]
+    return build_workload(name="tiny", kind=kind, dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv,
+                          head_dim=D, block_size=BS, rope_base=base, doc_lens=list(doc_lens),
+                          requests=requests, seed=seed, poison_tail=poison)
+
+
+# ---------------------------------------------------------------- rotation
+def test_rotation_is_complex_multiplication():
+    """rot(x, p) pairs (i, i+D/2) like x_i + j x_{i+D/2} multiplied by e^{j p theta_i}."""
+    D = 64
+    th = rope_theta(D, 1e4)
+    # Textbook RoPE frequencies, written independently: base^(-(0,2,4,..)/D).
+    th_ref = 1.0 / (1e4 ** (np.arange(0, D, 2, dtype=np.float64) / D))
+    np.testing.assert_allclose(th, th_ref, rtol=1e-15)
+    x = RNG.standard_normal((5, D))
+    pos = np.array([0, 1, 17, 4096, 131071])
+    z = (x[:, : D // 2] + 1j * x[:, D // 2:]) * np.exp(1j * pos[:, None] * th_ref[None, :])
+    ref = np.concatenate([z.real, z.imag], axis=1)
+    # complex exp and cos/sin round large angles (~1.3e5 rad) differently: ~1e-11
+    np.testing.assert_allclose(rope_rotate(x, pos, th), ref, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(rope_rotate(x[:3], pos[:3], th), ref[:3], rtol=0, atol=1e-13)
+
+
+def test_rotation_group_properties():
+    D = 128
+    th = rope_theta(D, 5e5)
+    x = RNG.standard_normal((3, D))
+    np.testing.assert_array_equal(rope_rotate(x, np.zeros(3), th), x)
+    for p in (1, 333, 65536):
+        y = rope_rotate(x, np.full(3, p), th)
+        np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    a, b = 1234, 4321
+    np.testing.assert_allclose(rope_rotate(rope_rotate(x, np.full(3, a), th), np.full(3, b), th),
+                               rope_rotate(x, np.full(3, a + b), th), atol=1e-10)
+
+
+@pytest.mark.parametrize("m,n", [(0, 5), (160, 3), (5184, 17), (131071, 65536), (7, 130000)])
+def test_fact_3_2_relative_rotation(m, n):
+    """(R_m q)^T (R_n k) = q^T R_{n-m} k  (LazyAttention §3.2, Fact 3.2)."""
+    D = 128
+    th = rope_theta(D, 5e5)
+    q = RNG.standard_normal(D)
+    k = RNG.standard_normal(D)
+    lhs = rope_rotate(q, m, th) @ rope_rotate(k, n, th)
+    rhs = q @ rope_rotate(k, n - m, th)
+    # angles reach ~1.3e5 rad; fp64 rounding of p*theta bounds the agreement
+    tol = 1e-12 if max(m, n) < 1000 else 1e-8
+    assert abs(lhs - rhs) <= tol * (1 + abs(lhs))
+
+
+# ------------------------------------------------------- lazy equals eager
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_lazy_equals_eager(dtype):
+    """The un-rotated pool + relative rotation equals the re-encoded cache (§1, §3.1)."""
+    w = _tiny(dtype=dtype)
+    th = rope_theta(w.head_dim, w.rope_base)
+    for r in range(w.batch):
+        kw = dict(block_size=w.block_size, num_kv_heads=w.num_kv_heads, theta=th, scale=w.scale)
+        o1, l1 = attention_decode(w.q[r], int(w.q_pos[r]), w.requests[r], w.k_pool, w.v_pool, **kw)
+        o2, l2 = attention_decode_relative(w.q[r], int(w.q_pos[r]), w.requests[r], w.k_pool,
+                                           w.v_pool, **kw)
+        np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+def _shifted(segs, c):
+    return [Segment(s.start + c, s.n_tokens, s.blocks, s.is_new) for s in segs]
+
+
+@pytest.mark.parametrize("c", [1, 777, 60000])
+def test_shift_invariance(c):
+    """Moving every position by a constant leaves all scores unchanged (Fact 3.2)."""
+    w = _tiny()
+    th = rope_theta(w.head_dim, w.rope_base)
+    kw = dict(block_size=w.block_size, num_kv_heads=w.num_kv_heads, theta=th, scale=w.scale)
+    for r in range(w.batch):
+        o1, l1 = attention_decode(w.q[r], int(w.q_pos[r]), w.requests[r], w.k_pool, w.v_pool, **kw)
+        o2, l2 = attention_decode(w.q[r], int(w.q_pos[r]) + c, _shifted(w.requests[r], c),
+                                  w.k_pool, w.v_pool, **kw)
+        np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-10)
+    wp = _tiny(kind="prefill")
+    for r in range(wp.batch):
+        a, b = wp.cu_q[r], wp.cu_q[r + 1]
+        kw2 = dict(block_size=wp.block_size, num_kv_heads=wp.num_kv_heads, theta=th, scale=wp.scale)
+        o1, _ = attention_prefill(wp.q[a:b], int(wp.q_pos[r]), wp.requests[r], wp.k_pool, wp.v_pool, **kw2)
+        o2, _ = attention_prefill(wp.q[a:b], int(wp.q_pos[r]) + c, _shifted(wp.requests[r], c),
+                                  wp.k_pool, wp.v_pool, **kw2)
+        np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-10)
+
+
+# ------------------------------------------- special cases = library routine
+def _sdpa(q, k, v, causal=False, mask=None):
+    """torch SDPA in float64 on CPU; q [Hq, T, D], k/v [Hkv, n, D]; GQA by torch."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))[None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m,
+                                                         is_causal=causal, enable_gqa=True)
+    return o[0].numpy()
+
+
+def _gathered_by_test(w, r, g):
+    """Independent gather for the test: walk the request token by token."""
+    ks, vs = [], []
+    for s in w.requests[r]:
+        for t in range(s.n_tokens):
+            b = int(s.blocks[t // w.block_size])
+            ks.append(w.values_f32(w.k_pool[b, g, t % w.block_size]))
+            vs.append(w.values_f32(w.v_pool[b, g, t % w.block_size]))
+    return np.array(ks, np.float64), np.array(vs, np.float64)
+
+
+def test_identity_table_is_textbook_attention():
+    """With no rotation (theta = 0) the result is softmax(q K^T / sqrt(D)) V with GQA."""
+    w = _tiny(Hq=6, Hkv=2)
+    zero = np.zeros(w.head_dim // 2)
+    for r in range(w.batch):
+        o, _ = attention_decode(w.q[r], int(w.q_pos[r]), w.requests[r], w.k_pool, w.v_pool,
+                                block_size=w.block_size, num_kv_heads=w.num_kv_heads,
+                                theta=zero, scale=w.scale)
+        K = np.stack([_gathered_by_test(w, r, g)[0] for g in range(w.num_kv_heads)])
+        V = np.stack([_gathered_by_test(w, r, g)[1] for g in range(w.num_kv_heads)])
+        q = w.values_f32(w.q[r]).astype(np.float64)[:, None, :]
+        ref = _sdpa(q, K, V)[:, 0, :]
+        np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def _rope_complex(x, pos, base):
+    D = x.shape[-1]
+    inv = 1.0 / (base ** (np.arange(0, D, 2, dtype=np.float64) / D))
+    z = (x[..., : D // 2] + 1j * x[..., D // 2:]) * np.exp(1j * pos[:, None] * inv[None, :])
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_contiguous_placement_is_causal_rope_attention(dtype):
+    """One request tiling [0, L) is standard causal RoPE attention over the sequence.
+
+    The test writes a contiguous key/value sequence into randomly permuted pool
+    blocks itself, so a wrong block/slot mapping in the oracle fails here.
+    """
+    Hq, Hkv, D, BS, base = 4, 2, 32, 4, 1e4
+    doc_lens, new = [10, 8, 5], 7
+    L = sum(doc_lens) + new
+    rng = np.random.default_rng(11)
+    Kseq = rng.standard_normal((Hkv, L, D)).astype(np.float32)
+    Vseq = rng.standard_normal((Hkv, L, D)).astype(np.float32)
+    Qseq = rng.standard_normal((Hq, L, D)).astype(np.float32)
+    # scatter into permuted blocks
+    seg_lens = doc_lens + [new]
+    nblk = sum((n + BS - 1) // BS for n in seg_lens)
+    perm = rng.permutation(nblk + 3)[:nblk]
+    kpool = np.zeros((nblk + 3, Hkv, BS, D), np.float32)
+    vpool = np.zeros_like(kpool)
+    segs, cur, bi = [], 0, 0
+    for i, n in enumerate(seg_lens):
+        nb = (n + BS - 1) // BS
+        blocks = perm[bi:bi + nb]
+        for t in range(n):
+            kpool[blocks[t // BS], :, t % BS] = Kseq[:, cur + t]
+            vpool[blocks[t // BS], :, t % BS] = Vseq[:, cur + t]
+        segs.append(Segment(cur, n, blocks, i == len(seg_lens) - 1))
+        cur += n
+        bi += nb
+    pos = np.arange(L, dtype=np.float64)
+    Qr = _rope_complex(Qseq.astype(np.float64), pos, base)
+    Kr = _rope_complex(Kseq.astype(np.float64), pos, base)
+    full = _sdpa(Qr, Kr, Vseq, causal=True)  # [Hq, L, D]
+    th = rope_theta(D, base)
+    q_new = np.transpose(Qseq[:, L - new:, :], (1, 0, 2))  # [T, Hq, D]
+    o, _ = attention_prefill(q_new, L - new, segs, kpool, vpool, block_size=BS,
+                             num_kv_heads=Hkv, theta=th, scale=1 / math.sqrt(D))
+    np.testing.assert_allclose(o, np.transpose(full[:, L - new:, :], (1, 0, 2)), rtol=0, atol=1e-12)
+    # decode: one more query at position L attends exactly the L listed keys
+    qd = rng.standard_normal((Hq, D)).astype(np.float32)
+    qdr = _rope_complex(qd.astype(np.float64)[:, None, :], np.array([float(L)]), base)
+    ref = _sdpa(qdr, Kr, Vseq)[:, 0, :]
+    od, _ = attention_decode(qd, L, [Segment(s.start, s.n_tokens, s.blocks, False) for s in segs],
+                             kpool, vpool, block_size=BS, num_kv_heads=Hkv, theta=th,
+                             scale=1 / math.sqrt(D))
+    np.testing.assert_allclose(od, ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------ softmax closed forms
+def test_single_key_returns_its_value():
+    D, BS = 8, 4
+    kp = RNG.standard_normal((1, 1, BS, D)).astype(np.float32)
+    vp = RNG.standard_normal((1, 1, BS, D)).astype(np.float32)
+    q = RNG.standard_normal((1, D)).astype(np.float32)
+    th = rope_theta(D, 1e4)
+    o, l = attention_decode(q, 9, [Segment(5, 1, np.array([0]), False)], kp, vp, block_size=BS,
+                            num_kv_heads=1, theta=th, scale=0.5)
+    np.testing.assert_allclose(o[0], vp[0, 0, 0], atol=1e-15)
+    # lse of one key is its score: 0.5 * q^T R_{5-9} k (complex-form rotation, relative)
+    qk = _rope_complex(q.astype(np.float64), np.array([9.0]), 1e4) @ \
+        _rope_complex(kp[0, 0, :1].astype(np.float64), np.array([5.0]), 1e4).T
+    assert abs(l[0] - 0.5 * qk[0, 0]) < 1e-12
+
+
+def test_zero_keys_average_values():
+    D, BS, n = 8, 4, 11
+    kp = np.zeros((3, 1, BS, D), np.float32)
+    vp = RNG.standard_normal((3, 1, BS, D)).astype(np.float32)
+    q = RNG.standard_normal((1, D)).astype(np.float32)
+    th = rope_theta(D, 1e4)
+    o, l = attention_decode(q, 40, [Segment(0, n, np.array([2, 0, 1]), False)], kp, vp,
+                            block_size=BS, num_kv_heads=1, theta=th, scale=1.0)
+    vals = np.concatenate([vp[2, 0], vp[0, 0], vp[1, 0]])[:n].astype(np.float64)
+    np.testing.assert_allclose(o[0], vals.mean(axis=0), atol=1e-14)
+    assert abs(l[0] - math.log(n)) < 1e-14
+
+
+def test_dominant_score_selects_value():
+    D, BS = 8, 4
+    kp = np.zeros((2, 1, BS, D), np.float32)
+    vp = RNG.standard_normal((2, 1, BS, D)).astype(np.float32)
+    kp[1, 0, 2, 0] = 1.0
+    q = np.zeros((1, D), np.float32)
+    q[0, 0] = 1.0
+    th = np.zeros(D // 2)  # identity rotation: the score of key (1,2) is 1e4 * 1
+    o, _ = attention_decode(q, 8, [Segment(0, 8, np.array([0, 1]), False)], kp, vp,
+                            block_size=BS, num_kv_heads=1, theta=th, scale=1e4)
+    np.testing.assert_allclose(o[0], vp[1, 0, 2], atol=1e-12)
+
+
+# ------------------------------------------------------------ brute force
+def _brute_case(w, r, qrows=None):
+    out = []
+    for h in range(w.num_q_heads):
+        g = h // w.group
+        keys = []
+        for s in w.requests[r]:
+            for t in range(s.n_tokens):
+                b = int(s.blocks[t // w.block_size])
+                keys.append((w.values_f32(w.k_pool[b, g, t % w.block_size]).tolist(),
+                             w.values_f32(w.v_pool[b, g, t % w.block_size]).tolist(),
+                             s.start + t, s.is_new))
+        if w.kind == "decode":
+            qs = [(w.values_f32(w.q[r, h]).tolist(), int(w.q_pos[r]))]
+        else:
+            a = int(w.cu_q[r])
+            qs = [(w.values_f32(w.q[a + j, h]).tolist(), int(w.q_pos[r]) + j)
+                  for j in range(w.q_len(r))]
+        out.append(brute_attention(qs, keys, w.scale, w.rope_base))
+    return out
+
+
+def test_brute_force_config1():
+    w = make_config(1)
+    ref = _brute_case(w, 0)
+    o, l = run_decode(w)[0]
+    np.testing.assert_allclose(o[0], ref[0][0][0], atol=1e-12)
+    assert abs(l[0] - ref[0][0][1]) < 1e-12
+    assert int(w.q_pos[0]) == 160 and w.keys_per_request()[0] == 160
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_brute_force_tiny_decode(dtype):
+    """Partial blocks, GQA 2, a document repeated at two offsets in one request."""
+    w = _tiny(dtype=dtype)
+    res = run_decode(w)
+    for r in range(w.batch):
+        ref = _brute_case(w, r)
+        for h in range(w.num_q_heads):
+            np.testing.assert_allclose(res[r][0][h], ref[h][0][0], atol=1e-12)
+            assert abs(res[r][1][h] - ref[h][0][1]) < 1e-12
+
+
+def test_brute_force_tiny_prefill():
+    w = _tiny(kind="prefill")
+    res = run_prefill(w)
+    for r in range(w.batch):
+        ref = _brute_case(w, r)
+        for h in range(w.num_q_heads):
+            for j in range(w.q_len(r)):
+                np.testing.assert_allclose(res[r][0][j, h], ref[h][j][0], atol=1e-12)
+                assert abs(res[r][1][j, h] - ref[h][j][1]) < 1e-12
+
+
+# --------------------------------------------------- zero-copy invariances
+def test_segment_order_and_block_relocation():
+    w = _tiny()
+    th = rope_theta(w.head_dim, w.rope_base)
+    kw = dict(block_size=w.block_size, num_kv_heads=w.num_kv_heads, theta=th, scale=w.scale)
+    r = 1
+    o1, _ = attention_decode(w.q[r], int(w.q_pos[r]), w.requests[r], w.k_pool, w.v_pool, **kw)
+    rev = list(reversed(w.requests[r]))
+    o2, _ = attention_decode(w.q[r], int(w.q_pos[r]), rev, w.k_pool, w.v_pool, **kw)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    # relocate every block of the request to fresh ids at the end of the pool
+    kp = np.concatenate([w.k_pool, w.k_pool])
+    vp = np.concatenate([w.v_pool, w.v_pool])
+    nb = w.num_blocks
+    moved = [Segment(s.start, s.n_tokens, s.blocks + nb, s.is_new) for s in w.requests[r]]
+    o3, _ = attention_decode(w.q[r], int(w.q_pos[r]), moved, kp, vp, **kw)
+    np.testing.assert_array_equal(o1, o3)
+
+
+def test_poisoned_tail_slots_are_never_read():
+    w = _tiny(poison=True)
+    for r, (o, l) in run_decode(w).items():
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+# -------------------------------------------------------- closed forms, Eq. 3
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def test_eq3_hit_ratio_gap_printed_value():
+    """2.86x at D=20, C=100 (§1, §2 Eq. 3); the printed alpha-free value needs alpha ~ 0.853."""
+    g = _golden()["eq3_hit_ratio_gap"]
+    gap = hit_ratio_gap(g["C"], g["D"], 0.853)
+    assert round(gap, 2) == g["printed_gap"]
+    # none of the skews printed elsewhere in the paper reproduces it
+    for a in (1.1, 1.5, 2.1):
+        assert round(hit_ratio_gap(g["C"], g["D"], a), 2) != g["printed_gap"]
+    # uniform popularity: the ratio of counts C / floor(C/D)
+    assert hit_ratio_gap(100, 20, 0.0) == pytest.approx(20.0, abs=1e-12)
+    gaps = [hit_ratio_gap(100, 20, a) for a in np.linspace(0, 3, 31)]
+    assert all(x > y for x, y in zip(gaps, gaps[1:]))
+
+
+@pytest.mark.parametrize("alpha", [1.1, 1.5, 2.1])
+def test_zipf_sums_match_hurwitz_zeta(alpha):
+    from scipy.special import zeta
+    for n in (1, 5, 100, 100000):
+        ref = zeta(alpha, 1) - zeta(alpha, n + 1)
+        assert zipf_partial_sum(n, alpha) == pytest.approx(ref, rel=1e-10)
+
+
+def test_cost_model_printed_percentages():
+    g = _golden()
+    for c in g["naive_flops_overhead"]["cases"]:
+        assert round(100 * naive_flops_overhead(c["M"]), 2) == c["printed_percent"]
+    (c,) = g["naive_io_overhead"]["cases"]
+    v = naive_io_overhead(c["M"], c["N"])
+    assert 0.95 < v < 1.0  # "approaching 100%"
+    (c,) = g["prefill_flops_overhead"]["cases"]
+    assert round(100 * prefill_flops_overhead(c["M"]), 2) == c["printed_percent"]
+    (c,) = g["prefill_table_bandwidth"]["cases"]
+    assert round(100 * prefill_table_bandwidth(c["N"]), 1) == c["printed_percent"]
+    (c,) = g["decode_trigger_overhead"]["cases"]
+    assert round(100 * decode_trigger_overhead(c["N"]), 2) == c["printed_percent"]
