@@ -1,0 +1,225 @@
+/*
+ * lazy_attn.h -- C ABI of the lazy-RoPE paged attention library (liblazyattn.so)
+ *
+ * Attention over a paged key/value block pool whose keys are stored WITHOUT
+ * positional encoding.  Rotary position embedding (RoPE) is applied inside the
+ * kernels at each request's logical positions, so one physical copy of a
+ * document's blocks serves any number of requests that place the document at
+ * different prompt offsets, and no re-encoded copy is ever written.  This is
+ * the deferred positional encoding of "LazyAttention: Efficient
+ * Retrieval-Augmented Generation with Deferred Positional Encoding"
+ * (§1 and §3.1 "Deferred encoding"; problem statement of §3: the same
+ * document at different offsets within one batch).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All functions return la_status and never throw.  On failure
+ *    lazy_attn_last_error() returns a message for the calling thread.
+ *  - Pointers marked "device" are GPU memory owned by the caller; "host"
+ *    pointers are CPU memory owned by the caller.  The library allocates no
+ *    device memory and keeps no state besides the per-thread error message.
+ *  - GPU entry points enqueue work on the caller's stream (a hipStream_t passed
+ *    as void*, NULL = default stream) and return without synchronising.
+ *    Scalar arguments are checked before anything is enqueued; the contents of
+ *    device arrays are NOT checked on the device (use the host-side
+ *    lazy_attn_pack_segments / lazy_attn_validate_table for that).  Malformed
+ *    device tables give undefined results.
+ *  - Calls are thread-safe; concurrent calls on one stream serialise in order.
+ *
+ * RoPE convention (readings of the paper, stated once here)
+ * ---------------------------------------------------------
+ *  Feature pair (i, i + D/2), i < D/2, is rotated by angle p * theta_i with
+ *  theta_i = base^(-2i/D):  y_i = x_i cos - x_{i+D/2} sin,
+ *  y_{i+D/2} = x_i sin + x_{i+D/2} cos  (§3.2 "Prefilling", rotation over the
+ *  two half-dimensions).  The score of a query at position m and a key at
+ *  position p is scale * (R_m q)^T (R_p k) = scale * q^T R_{p-m} k (§3.2,
+ *  Fact 3.2).  Query head h reads kv head h / (num_q_heads / num_kv_heads)
+ *  (§3.5 "GQA/MQA").
+ *
+ * Data layouts (row-major, contiguous)
+ * ------------------------------------
+ *  k_pool   [num_blocks][num_kv_heads][block_size][head_dim]   un-rotated K
+ *  v_pool   [num_blocks][num_kv_heads][head_dim][block_size]   V, dim-major
+ *           inside each (block, kv head) tile, so the token axis -- the
+ *           contraction axis of P.V -- is contiguous.
+ *  cos_sin  float32 [max_pos][2][head_dim/2]: row p holds cos(p theta_i) then
+ *           sin(p theta_i).  Build it with lazy_attn_rope_table (float64
+ *           arithmetic, rounded once to float32).  Always float32.
+ *  q / out  decode:  [batch][num_q_heads][head_dim]
+ *           prefill: [total_q][num_q_heads][head_dim], rows cu_q[r] ..
+ *           cu_q[r+1]-1 are request r's new tokens.
+ *           Element type is bf16 (LA_BF16) or float32 (LA_FP32, test mode) for
+ *           q, out, k_pool and v_pool alike.
+ *  lse      float32, [batch][num_q_heads] or [total_q][num_q_heads], natural
+ *           log of the softmax denominator including the max; nullable.
+ *
+ * Block table (per request, CSR)
+ * ------------------------------
+ *  blk_words[req_blk_start[r] .. req_blk_start[r+1]-1] describe request r's
+ *  blocks, in any order.  Each 64-bit word packs (§3.2 "Decoding": block id,
+ *  offset and mask bit-packed into one 64-bit register):
+ *     bits  0..31  physical block id
+ *     bits 32..55  pos0: logical position of the block's slot 0
+ *     bits 56..62  n_valid - 1: slots 0 .. n_valid-1 hold tokens
+ *     bit  63      causal: the block holds new prompt tokens of a prefill
+ *                  request; its key at position p is visible to a query at
+ *                  position m only when p <= m.  Ignored by decode.
+ *  Slot i of a block is the token at logical position pos0 + i.
+ */
+#ifndef LAZY_ATTN_H
+#define LAZY_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define LA_API __attribute__((visibility("default")))
+#else
+#define LA_API
+#endif
+
+typedef enum la_status {
+  LA_OK = 0,
+  LA_ERR_INVALID_ARG = 1,         /* null pointer, bad size, malformed table */
+  LA_ERR_UNSUPPORTED = 2,         /* head_dim / block_size / dtype / group not built */
+  LA_ERR_WORKSPACE_TOO_SMALL = 3, /* decode workspace below the queried size */
+  LA_ERR_HIP = 4                  /* HIP runtime error (incl. no device) */
+} la_status;
+
+typedef enum la_dtype { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
+
+/* Packing limits of the 64-bit block word. */
+#define LA_MAX_POSITION ((int64_t)1 << 24) /* positions must be < 2^24 */
+#define LA_MAX_BLOCK_ID ((int64_t)1 << 32)
+
+typedef struct la_params {
+  int32_t num_q_heads;   /* Hq; a multiple of num_kv_heads */
+  int32_t num_kv_heads;  /* Hkv */
+  int32_t head_dim;      /* D: 128 (bf16 and fp32) or 64 (fp32 only) */
+  int32_t block_size;    /* tokens per block: 16 */
+  int64_t num_blocks;    /* blocks in the pool */
+  int32_t dtype;         /* la_dtype of q, out, k_pool, v_pool */
+  float scale;           /* multiplies q.k; usually 1/sqrt(head_dim) */
+  int32_t max_pos;       /* rows of cos_sin; every position must be < max_pos */
+  int32_t split_blocks;  /* decode: blocks per split group, 0 = automatic */
+  int32_t target_workgroups; /* decode split heuristic, 0 = 1024 (256 CUs x 4) */
+  int32_t reserved[5];   /* must be zero */
+} la_params;
+
+/* Human-readable name of a status code (static string). */
+LA_API const char* lazy_attn_status_string(la_status s);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+LA_API const char* lazy_attn_last_error(void);
+
+/*
+ * Fill a host cos/sin table: out[p][0][i] = cos(p theta_i),
+ * out[p][1][i] = sin(p theta_i), theta_i = base^(-2i/head_dim), computed in
+ * float64 and rounded once to float32 (stateless per row: no incremental
+ * rotation updates, so no error accumulates along positions -- App. C.4).
+ *   base      RoPE base (> 1), e.g. 10000 or 500000
+ *   head_dim  even, 2 .. 1024
+ *   rows      number of positions (>= 1)
+ *   out       host, rows * head_dim floats
+ */
+LA_API la_status lazy_attn_rope_table(double base, int32_t head_dim, int32_t rows, float* out);
+
+/*
+ * Pack per-request segment lists into block words (host only).
+ * A segment is a run of n tokens at logical positions start .. start+n-1 whose
+ * token t lives in block blocks[t / block_size], slot t % block_size.
+ *   batch           number of requests (>= 1)
+ *   req_seg_start   host [batch+1]: request r owns segments req_seg_start[r] ..
+ *   seg_start       host [S] logical position of each segment's token 0
+ *   seg_len         host [S] tokens per segment (>= 1)
+ *   seg_is_new      host [S] 1 = new prompt tokens (causal), 0 = cached
+ *   seg_blk_start   host [S+1]: segment s owns seg_blocks[seg_blk_start[s] ..]
+ *   seg_blocks      host block ids; a segment needs ceil(len/block_size) of them
+ *   blk_words       host out [capacity]
+ *   req_blk_start   host out [batch+1]
+ *   max_blocks_per_req  host out (nullable): largest per-request block count
+ * Checks block ids < num_blocks, positions < min(max_pos, 2^24), block counts,
+ * and that every request has at least one token.  Returns LA_ERR_INVALID_ARG
+ * (nothing written beyond what was checked) on violation.
+ */
+LA_API la_status lazy_attn_pack_segments(const la_params* p, int32_t batch, const int64_t* req_seg_start,
+                                  const int64_t* seg_start, const int64_t* seg_len,
+                                  const uint8_t* seg_is_new, const int64_t* seg_blk_start,
+                                  const int64_t* seg_blocks, uint64_t* blk_words,
+                                  int64_t capacity, int32_t* req_blk_start,
+                                  int32_t* max_blocks_per_req);
+
+/*
+ * Check a packed table against the pool and position limits (debug helper).
+ * Arrays may be host or device memory (device ones are copied synchronously).
+ *   q_pos   decode: query position per request; prefill: position of the
+ *           first new token per request
+ *   cu_q    prefill: [batch+1] query row offsets; NULL for decode
+ * Decode requires every key position < max_pos and q_pos < max_pos; prefill
+ * requires q_pos + (cu_q[r+1]-cu_q[r]) - 1 < max_pos and that each new-token
+ * row sees at least one key.
+ */
+LA_API la_status lazy_attn_validate_table(const la_params* p, int32_t batch, const uint64_t* blk_words,
+                                   const int32_t* req_blk_start, const int32_t* q_pos,
+                                   const int32_t* cu_q);
+
+/*
+ * Bytes of device workspace lazy_attn_decode needs for this shape (0 when the
+ * split heuristic keeps one split group per (request, kv head)).  Depends only
+ * on the arguments, not on the device.
+ */
+LA_API la_status lazy_attn_decode_workspace_size(const la_params* p, int32_t batch,
+                                          int32_t max_blocks_per_req, size_t* bytes);
+
+/*
+ * Decode: one new query token per request attends exactly the request's
+ * listed keys (§3.2 "Decoding"; §3.4 decode roofline: only K and V are read).
+ *   q              device [batch][Hq][D]
+ *   k_pool/v_pool  device, layouts above
+ *   blk_words      device packed words; req_blk_start device [batch+1]
+ *   q_pos          device [batch] logical position m of each query
+ *   cos_sin        device [max_pos][2][D/2] float32
+ *   max_blocks_per_req  host scalar: upper bound of per-request block counts
+ *   out            device [batch][Hq][D] (same dtype as q)
+ *   lse            device [batch][Hq] float32 or NULL
+ *   workspace      device, >= lazy_attn_decode_workspace_size bytes (may be
+ *                  NULL when that size is 0); clobbered
+ * Requires every key position p and m in [0, max_pos) and every request
+ * non-empty.  bf16 mode needs head_dim 128, block_size 16 and a group size
+ * Hq/Hkv in {1, 2, 4, 8, 16}; fp32 mode needs head_dim 64 or 128.
+ */
+LA_API la_status lazy_attn_decode(const la_params* p, const void* q, const void* k_pool,
+                           const void* v_pool, const uint64_t* blk_words,
+                           const int32_t* req_blk_start, const int32_t* q_pos,
+                           const float* cos_sin, int32_t batch, int32_t max_blocks_per_req,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * Prefill: the new prompt tokens of each request attend every cached key of
+ * the request and, among the new tokens, causally (§3.2 "Prefilling"; §3.4
+ * Eq. 7 TTFT model: attention of the L' new tokens against all L keys).
+ *   q          device [total_q][Hq][D]; cu_q device [batch+1]
+ *   q_pos0     device [batch]: logical position of request r's first new
+ *              token; new token j sits at q_pos0[r] + j
+ *   max_q_per_req  host scalar: upper bound of cu_q[r+1] - cu_q[r]
+ *   out        device [total_q][Hq][D]; lse device [total_q][Hq] or NULL
+ * The new tokens' own K/V must already be in the pool, in blocks flagged
+ * causal.  Every query row must see at least one key.  bf16 mode needs
+ * head_dim 128, block_size 16, group size in {1, 2, 4, 8, 16}.
+ */
+LA_API la_status lazy_attn_prefill(const la_params* p, const void* q, const void* k_pool,
+                            const void* v_pool, const uint64_t* blk_words,
+                            const int32_t* req_blk_start, const int32_t* cu_q,
+                            const int32_t* q_pos0, const float* cos_sin, int32_t batch,
+                            int32_t max_q_per_req, void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* LAZY_ATTN_H */

@@ -1,0 +1,23 @@
+"""Lazy-RoPE paged attention on MI355X (gfx950).
+
+liblazyattn.so (HIP kernels + C ABI, include/lazy_attn.h) computes attention
+over a key/value block pool stored without positional encoding, applying RoPE
+inside the kernels at each request's logical positions.  This package holds
+the HIP sources (csrc/), the build script and a thin ctypes binding whose
+functions carry the C names.
+"""
+from .binding import (  # noqa: F401
+    LA_BF16,
+    LA_FP32,
+    LazyAttnError,
+    la_params,
+    make_params,
+    lazy_attn_status_string,
+    lazy_attn_last_error,
+    lazy_attn_rope_table,
+    lazy_attn_pack_segments,
+    lazy_attn_validate_table,
+    lazy_attn_decode_workspace_size,
+    lazy_attn_decode,
+    lazy_attn_prefill,
+)

@@ -1,0 +1,224 @@
+"""ctypes binding of liblazyattn.so (the C ABI in include/lazy_attn.h).
+
+Argument marshalling only: every function forwards to the C entry point of
+the same name.  Device arguments are torch tensors (their data_ptr() is
+passed) and the stream is a torch.cuda.Stream or a raw hipStream_t integer.
+There is no fallback: if the library is missing, importing this module
+raises, and every non-OK status raises LazyAttnError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("LAZYATTN_LIB", os.path.join(_PKG, "liblazyattn.so"))
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} not found: build it with `python -m position_agnostic_kv_lazy_amd.build` "
+        "(or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE_TOO_SMALL, LA_ERR_HIP = range(5)
+LA_BF16, LA_FP32 = 0, 1
+
+EXPORTED = (
+    "lazy_attn_status_string",
+    "lazy_attn_last_error",
+    "lazy_attn_rope_table",
+    "lazy_attn_pack_segments",
+    "lazy_attn_validate_table",
+    "lazy_attn_decode_workspace_size",
+    "lazy_attn_decode",
+    "lazy_attn_prefill",
+)
+
+
+class la_params(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("max_pos", ctypes.c_int32),
+        ("split_blocks", ctypes.c_int32),
+        ("target_workgroups", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 5),
+    ]
+
+
+class LazyAttnError(RuntimeError):
+    def __init__(self, status: int, func: str):
+        self.status = status
+        msg = _lib.lazy_attn_last_error().decode()
+        name = _lib.lazy_attn_status_string(status).decode()
+        super().__init__(f"{func}: {name}: {msg}")
+
+
+_P = ctypes.c_void_p
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_prm = ctypes.POINTER(la_params)
+
+_lib.lazy_attn_status_string.restype = ctypes.c_char_p
+_lib.lazy_attn_status_string.argtypes = [ctypes.c_int]
+_lib.lazy_attn_last_error.restype = ctypes.c_char_p
+_lib.lazy_attn_last_error.argtypes = []
+_lib.lazy_attn_rope_table.restype = ctypes.c_int
+_lib.lazy_attn_rope_table.argtypes = [ctypes.c_double, ctypes.c_int32, ctypes.c_int32, _f32p]
+_lib.lazy_attn_pack_segments.restype = ctypes.c_int
+_lib.lazy_attn_pack_segments.argtypes = [_prm, ctypes.c_int32, _i64p, _i64p, _i64p, _u8p, _i64p,
+                                         _i64p, _u64p, ctypes.c_int64, _i32p, _i32p]
+_lib.lazy_attn_validate_table.restype = ctypes.c_int
+_lib.lazy_attn_validate_table.argtypes = [_prm, ctypes.c_int32, _P, _P, _P, _P]
+_lib.lazy_attn_decode_workspace_size.restype = ctypes.c_int
+_lib.lazy_attn_decode_workspace_size.argtypes = [_prm, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+_lib.lazy_attn_decode.restype = ctypes.c_int
+_lib.lazy_attn_decode.argtypes = [_prm, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                  _P, _P, _P, ctypes.c_size_t, _P]
+_lib.lazy_attn_prefill.restype = ctypes.c_int
+_lib.lazy_attn_prefill.argtypes = [_prm, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                   ctypes.c_int32, _P, _P, _P]
+
+
+def _check(status: int, func: str):
+    if status != LA_OK:
+        raise LazyAttnError(status, func)
+
+
+def make_params(*, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, scale,
+                max_pos, split_blocks=0, target_workgroups=0) -> la_params:
+    p = la_params()
+    p.num_q_heads = num_q_heads
+    p.num_kv_heads = num_kv_heads
+    p.head_dim = head_dim
+    p.block_size = block_size
+    p.num_blocks = num_blocks
+    p.dtype = {"bf16": LA_BF16, "f32": LA_FP32}.get(dtype, dtype)
+    p.scale = scale
+    p.max_pos = max_pos
+    p.split_blocks = split_blocks
+    p.target_workgroups = target_workgroups
+    return p
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a tensor (None passes NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def lazy_attn_status_string(status: int) -> str:
+    return _lib.lazy_attn_status_string(status).decode()
+
+
+def lazy_attn_last_error() -> str:
+    return _lib.lazy_attn_last_error().decode()
+
+
+def lazy_attn_rope_table(base: float, head_dim: int, rows: int) -> np.ndarray:
+    """Host float32 table [rows, head_dim] (cos half, then sin half)."""
+    out = np.empty((rows, head_dim), dtype=np.float32)
+    _check(_lib.lazy_attn_rope_table(float(base), head_dim, rows,
+                                     out.ctypes.data_as(_f32p)), "lazy_attn_rope_table")
+    return out
+
+
+def lazy_attn_pack_segments(params: la_params, requests: Sequence[Sequence]):
+    """Pack segment lists into (blk_words uint64, req_blk_start int32, max_blocks).
+
+    requests[r] is a sequence of segments with attributes start, n_tokens,
+    blocks and is_new (or tuples in that order).
+    """
+    req_seg, starts, lens, news, blk_start, blocks = [0], [], [], [], [0], []
+    for segs in requests:
+        for s in segs:
+            st, n, bl, nw = (s.start, s.n_tokens, s.blocks, s.is_new) if hasattr(s, "start") else s
+            starts.append(int(st))
+            lens.append(int(n))
+            news.append(1 if nw else 0)
+            bl = np.asarray(bl, dtype=np.int64).ravel()
+            blocks.append(bl)
+            blk_start.append(blk_start[-1] + len(bl))
+        req_seg.append(len(starts))
+    a_req = np.asarray(req_seg, np.int64)
+    a_st = np.asarray(starts, np.int64)
+    a_len = np.asarray(lens, np.int64)
+    a_new = np.asarray(news, np.uint8)
+    a_bs = np.asarray(blk_start, np.int64)
+    a_bl = np.concatenate(blocks).astype(np.int64) if blocks else np.zeros(0, np.int64)
+    cap = max(1, int(a_bs[-1]))
+    words = np.zeros(cap, np.uint64)
+    rbs = np.zeros(len(requests) + 1, np.int32)
+    maxb = ctypes.c_int32(0)
+    _check(_lib.lazy_attn_pack_segments(
+        ctypes.byref(params), len(requests), a_req.ctypes.data_as(_i64p),
+        a_st.ctypes.data_as(_i64p), a_len.ctypes.data_as(_i64p), a_new.ctypes.data_as(_u8p),
+        a_bs.ctypes.data_as(_i64p), a_bl.ctypes.data_as(_i64p), words.ctypes.data_as(_u64p), cap,
+        rbs.ctypes.data_as(_i32p), ctypes.byref(maxb)), "lazy_attn_pack_segments")
+    return words[: int(rbs[-1])], rbs, int(maxb.value)
+
+
+def _hptr(x):
+    """Pointer for host numpy arrays or device tensors."""
+    if x is None:
+        return None
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    return _ptr(x)
+
+
+def lazy_attn_validate_table(params: la_params, batch: int, blk_words, req_blk_start, q_pos,
+                             cu_q=None):
+    _check(_lib.lazy_attn_validate_table(ctypes.byref(params), batch, _hptr(blk_words),
+                                         _hptr(req_blk_start), _hptr(q_pos), _hptr(cu_q)),
+           "lazy_attn_validate_table")
+
+
+def lazy_attn_decode_workspace_size(params: la_params, batch: int, max_blocks_per_req: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.lazy_attn_decode_workspace_size(ctypes.byref(params), batch, max_blocks_per_req,
+                                                ctypes.byref(n)), "lazy_attn_decode_workspace_size")
+    return int(n.value)
+
+
+def lazy_attn_decode(params: la_params, q, k_pool, v_pool, blk_words, req_blk_start, q_pos,
+                     cos_sin, batch: int, max_blocks_per_req: int, out, lse=None, workspace=None,
+                     stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.lazy_attn_decode(ctypes.byref(params), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                 _ptr(blk_words), _ptr(req_blk_start), _ptr(q_pos), _ptr(cos_sin),
+                                 batch, max_blocks_per_req, _ptr(out), _ptr(lse), _ptr(workspace),
+                                 ws_bytes, _stream(stream)), "lazy_attn_decode")
+
+
+def lazy_attn_prefill(params: la_params, q, k_pool, v_pool, blk_words, req_blk_start, cu_q,
+                      q_pos0, cos_sin, batch: int, max_q_per_req: int, out, lse=None,
+                      stream=None):
+    _check(_lib.lazy_attn_prefill(ctypes.byref(params), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                  _ptr(blk_words), _ptr(req_blk_start), _ptr(cu_q), _ptr(q_pos0),
+                                  _ptr(cos_sin), batch, max_q_per_req, _ptr(out), _ptr(lse),
+                                  _stream(stream)), "lazy_attn_prefill")

@@ -1,0 +1,112 @@
+// fp32 test-mode attention over the position-free paged pool.
+//
+// Deliberately simple: one wave per (query row, query head); lane i owns the
+// RoPE feature pair (i, i + D/2).  Every key is rotated to its own logical
+// position from the cos/sin table (the eager form of deferred encoding,
+// "LazyAttention" §3.1), the query to its position, and an online softmax in
+// fp32 accumulates the output.  Used for the 1e-5 parity mode; the bf16
+// kernels are the fast path.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace lazyattn {
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k_pool,
+    const float* __restrict__ v_pool, const uint64_t* __restrict__ words,
+    const int32_t* __restrict__ req_blk_start, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ q_pos, const float* __restrict__ cs, int Hq, int Hkv, int BS,
+    float scale, float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int HALF = D / 2;
+  const int h = blockIdx.x;
+  const int r = blockIdx.z;
+  const int lane = threadIdx.x;
+  int row, qp;
+  if (cu_q != nullptr) {  // prefill: blockIdx.y is the new-token index
+    const int j = blockIdx.y;
+    const int a = cu_q[r];
+    if (j >= cu_q[r + 1] - a) return;
+    row = a + j;
+    qp = q_pos[r] + j;
+  } else {
+    row = r;
+    qp = q_pos[r];
+  }
+  const int g = h / (Hq / Hkv);
+  const bool active = lane < HALF;
+  const int i = active ? lane : 0;
+
+  // Query rotated to its own position m.
+  const float* qrow = q + (static_cast<size_t>(row) * Hq + h) * D;
+  float q1 = 0.f, q2 = 0.f;
+  if (active) {
+    const float x1 = qrow[i], x2 = qrow[i + HALF];
+    const float c = cs[static_cast<size_t>(qp) * D + i];
+    const float s = cs[static_cast<size_t>(qp) * D + HALF + i];
+    q1 = x1 * c - x2 * s;
+    q2 = x1 * s + x2 * c;
+  }
+
+  float m = -INFINITY, l = 0.f, acc1 = 0.f, acc2 = 0.f;
+  const int b_end = req_blk_start[r + 1];
+  for (int b = req_blk_start[r]; b < b_end; ++b) {
+    const BlockWord w = unpack_word(words[b]);
+    const size_t tile = static_cast<size_t>(w.block_id) * Hkv + g;
+    const float* kb = k_pool + tile * BS * D;
+    const float* vb = v_pool + tile * D * BS;
+    for (int t = 0; t < w.n_valid; ++t) {
+      const int p = w.pos0 + t;
+      if (cu_q != nullptr && w.causal && p > qp) break;  // later slots are later positions
+      float part = 0.f, v1 = 0.f, v2 = 0.f;
+      if (active) {
+        const float k1 = kb[t * D + i], k2 = kb[t * D + i + HALF];
+        const float c = cs[static_cast<size_t>(p) * D + i];
+        const float s = cs[static_cast<size_t>(p) * D + HALF + i];
+        part = q1 * (k1 * c - k2 * s) + q2 * (k1 * s + k2 * c);
+        v1 = vb[i * BS + t];
+        v2 = vb[(i + HALF) * BS + t];
+      }
+      const float sc = wave_sum(part) * scale;
+      const float mn = fmaxf(m, sc);
+      const float corr = expf(m - mn);
+      const float pe = expf(sc - mn);
+      l = l * corr + pe;
+      acc1 = acc1 * corr + pe * v1;
+      acc2 = acc2 * corr + pe * v2;
+      m = mn;
+    }
+  }
+  float* orow = out + (static_cast<size_t>(row) * Hq + h) * D;
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  if (active) {
+    orow[i] = acc1 * inv;
+    orow[i + HALF] = acc2 * inv;
+  }
+  if (lse != nullptr && lane == 0) lse[static_cast<size_t>(row) * Hq + h] = m + logf(l);
+}
+
+}  // namespace
+
+hipError_t launch_attn_f32(const AttnArgs& a, bool prefill, hipStream_t stream) {
+  const dim3 grid(a.num_q_heads, prefill ? a.max_q_per_req : 1, a.batch);
+  const int32_t* cu = prefill ? a.cu_q : nullptr;
+#define LAZYATTN_F32(DIM)                                                                    \
+  hipLaunchKernelGGL(attn_f32_kernel<DIM>, grid, dim3(64), 0, stream,                        \
+                     static_cast<const float*>(a.q), static_cast<const float*>(a.k_pool),    \
+                     static_cast<const float*>(a.v_pool), a.words, a.req_blk_start, cu,      \
+                     a.q_pos, a.cos_sin, a.num_q_heads, a.num_kv_heads, a.block_size,         \
+                     a.scale, static_cast<float*>(a.out), a.lse)
+  if (a.head_dim == 128) {
+    LAZYATTN_F32(128);
+  } else if (a.head_dim == 64) {
+    LAZYATTN_F32(64);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef LAZYATTN_F32
+  return hipGetLastError();
+}
+
+}  // namespace lazyattn

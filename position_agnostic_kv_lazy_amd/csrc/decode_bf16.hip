@@ -1,0 +1,377 @@
+// bf16 split-KV decode over the position-free paged pool (gfx950).
+//
+// Deferred RoPE ("LazyAttention" §3.2 "Decoding", Fact 3.2).  The pool holds
+// un-rotated keys, so every key needs its own rotation.  The score of query
+// position m and key slot i of a block whose slot 0 sits at pos0 is
+//     (R_m q)^T (R_{pos0+i} k) = (R_{m-pos0} q)^T (R_i k),
+// so the kernel
+//   * rotates q once per block by m - pos0 (one cos/sin row per block, shared
+//     by the 16 keys of the block; rows are L2-resident), and
+//   * rotates each key by its in-block slot i in [0, 16): a lane always owns
+//     the same slot, so its 16 cos/sin pairs stay in registers for the whole
+//     kernel and the key stream costs no table traffic at all.
+// This keeps the paper's "no extra I/O in the decode inner loop" property
+// (§3.4: decode time ~ 2LD / bandwidth) for a pool with no positions in it.
+//
+// Work decomposition: workgroup = 4 waves = one split group of one (request,
+// kv head); the waves take the group's blocks round-robin and merge their
+// online-softmax states through LDS.  With one split group per (request, kv
+// head) the workgroup writes the final bf16 output; otherwise it writes an
+// fp32 partial (o, m, l) and a small combine kernel merges the groups.
+//
+// Per block (16 keys x 128 dims, K and V 4 KB each) and wave:
+//   S^T[16 keys x 16 cols] = K' Q_b^T   4 x v_mfma_f32_16x16x32_bf16
+//       (cols = the G query heads of the kv head, zero-padded to 16)
+//   O^T[128 dims x 16 cols] += V^T P^T   8 x v_mfma_f32_16x16x16_bf16
+// The S^T accumulator layout (lane = column, 4 consecutive keys per lane) is
+// exactly the B-operand layout of the P.V product, so P never leaves the lane.
+// V tiles are stored dim-major in the pool so the A operand of P.V (4
+// consecutive keys of one dim) is one 8-byte load.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace lazyattn {
+namespace {
+
+constexpr int D = 128;
+constexpr int HALF = 64;
+constexpr int BS = 16;
+constexpr int WAVES = 4;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ i16x4 as_i16x4(uint2 u) { return __builtin_bit_cast(i16x4, u); }
+
+template <int G>
+__global__ __launch_bounds__(256) void decode_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
+    const uint16_t* __restrict__ v_pool, const uint64_t* __restrict__ words,
+    const int32_t* __restrict__ req_blk_start, const int32_t* __restrict__ q_pos,
+    const float* __restrict__ cs, int Hkv, int npairs, int groups, int group_blocks,
+    float qscale, float* __restrict__ part_o, float* __restrict__ part_ml,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  static_assert(G >= 1 && G <= 16 && 64 % G == 0, "group size");
+  constexpr int LPH = 64 / G;  // rotation lanes per query head
+  const int Hq = Hkv * G;
+  const int pair = blockIdx.x % npairs;  // r * Hkv + g: same g -> same XCD
+  const int sg = blockIdx.x / npairs;
+  const int r = pair / Hkv;
+  const int g = pair - r * Hkv;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;   // MFMA column/row index: key slot (K) or head (Q)
+  const int gq = lane >> 4;  // MFMA k-group
+
+  __shared__ __attribute__((aligned(16))) uint16_t qb_lds[WAVES][G][D];
+  __shared__ float mo_lds[WAVES][G][D];
+  __shared__ float mm_lds[WAVES][G];
+  __shared__ float ml_lds[WAVES][G];
+
+  const int rb0 = req_blk_start[r];
+  const int rb1 = req_blk_start[r + 1];
+  const int gb0 = rb0 + sg * group_blocks;
+  const int gb1 = min(rb1, gb0 + group_blocks);
+  const int m = q_pos[r];
+
+  // Slot rotation of the key slot this lane owns: pairs j = 8*(4s+gq) + e.
+  float cslot[2][8], sslot[2][8];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const float* row = cs + static_cast<size_t>(n) * D + 8 * (4 * s + gq);
+    const float4 c0 = *reinterpret_cast<const float4*>(row);
+    const float4 c1 = *reinterpret_cast<const float4*>(row + 4);
+    const float4 s0 = *reinterpret_cast<const float4*>(row + HALF);
+    const float4 s1 = *reinterpret_cast<const float4*>(row + HALF + 4);
+    cslot[s][0] = c0.x; cslot[s][1] = c0.y; cslot[s][2] = c0.z; cslot[s][3] = c0.w;
+    cslot[s][4] = c1.x; cslot[s][5] = c1.y; cslot[s][6] = c1.z; cslot[s][7] = c1.w;
+    sslot[s][0] = s0.x; sslot[s][1] = s0.y; sslot[s][2] = s0.z; sslot[s][3] = s0.w;
+    sslot[s][4] = s1.x; sslot[s][5] = s1.y; sslot[s][6] = s1.z; sslot[s][7] = s1.w;
+  }
+
+  // Query values for the per-block rotation: lane -> (head hh, pairs pg*G + u).
+  const int hh = lane / LPH;
+  const int pg = lane - hh * LPH;
+  float qx1[G], qx2[G];
+  {
+    const uint16_t* qrow = q + (static_cast<size_t>(r) * Hq + g * G + hh) * D + pg * G;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      qx1[u] = __uint_as_float(static_cast<uint32_t>(qrow[u]) << 16) * qscale;
+      qx2[u] = __uint_as_float(static_cast<uint32_t>(qrow[HALF + u]) << 16) * qscale;
+    }
+  }
+
+  float mrun = -INFINITY, lrun = 0.f;
+  f32x4 oacc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int b = gb0 + wave; b < gb1; b += WAVES) {
+    const BlockWord w = unpack_word(words[b]);
+    const size_t tile = static_cast<size_t>(w.block_id) * Hkv + g;
+    // Issue the K and V loads first (4 x 16 B and 8 x 8 B per lane).
+    const uint16_t* kb = k_pool + tile * (BS * D) + n * D;
+    uint4 kr[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kr[s] = *reinterpret_cast<const uint4*>(kb + 8 * (4 * s + gq));
+    const uint16_t* vb = v_pool + tile * (D * BS) + n * BS + 4 * gq;
+    uint2 vr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vr[j] = *reinterpret_cast<const uint2*>(vb + 16 * j * BS);
+
+    // q_b = R_{m - pos0} q for this block; R_{-x} has the sine negated.
+    int off = m - w.pos0;
+    float sgn = 1.f;
+    if (off < 0) {
+      off = -off;
+      sgn = -1.f;
+    }
+    {
+      const float* row = cs + static_cast<size_t>(off) * D + pg * G;
+      uint16_t* dst = &qb_lds[wave][hh][0];
+#pragma unroll
+      for (int u = 0; u < G; u += 2) {
+        float y1[2], y2[2];
+#pragma unroll
+        for (int t = 0; t < 2 && u + t < G; ++t) {
+          const float c = row[u + t];
+          const float sn = sgn * row[HALF + u + t];
+          y1[t] = qx1[u + t] * c - qx2[u + t] * sn;
+          y2[t] = qx1[u + t] * sn + qx2[u + t] * c;
+        }
+        if (G == 1) {
+          dst[pg * G + u] = f32_to_bf16(y1[0]);
+          dst[HALF + pg * G + u] = f32_to_bf16(y2[0]);
+        } else {
+          *reinterpret_cast<uint32_t*>(dst + pg * G + u) = pack_bf16x2(y1[0], y1[1]);
+          *reinterpret_cast<uint32_t*>(dst + HALF + pg * G + u) = pack_bf16x2(y2[0], y2[1]);
+        }
+      }
+    }
+
+    // K' = R_slot k (fp32), rounded to bf16 for the MFMA.
+    bf16x8 ka[4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&kr[s]);
+      const uint32_t* a2 = reinterpret_cast<const uint32_t*>(&kr[s + 2]);
+      uint4 o1, o2;
+      uint32_t* p1 = reinterpret_cast<uint32_t*>(&o1);
+      uint32_t* p2 = reinterpret_cast<uint32_t*>(&o2);
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float y1[2], y2[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int e = 2 * e2 + t;
+          const float k1 = t ? bf16_hi(a1[e2]) : bf16_lo(a1[e2]);
+          const float k2 = t ? bf16_hi(a2[e2]) : bf16_lo(a2[e2]);
+          y1[t] = k1 * cslot[s][e] - k2 * sslot[s][e];
+          y2[t] = k1 * sslot[s][e] + k2 * cslot[s][e];
+        }
+        p1[e2] = pack_bf16x2(y1[0], y1[1]);
+        p2[e2] = pack_bf16x2(y2[0], y2[1]);
+      }
+      ka[s] = as_bf16x8(o1);
+      ka[s + 2] = as_bf16x8(o2);
+    }
+
+    // Q_b^T as the B operand: column n = head n (zero beyond G).
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    bf16x8 qbv[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint4 v = uint4{0u, 0u, 0u, 0u};
+      if (n < G) v = *reinterpret_cast<const uint4*>(&qb_lds[wave][n < G ? n : 0][8 * (4 * s + gq)]);
+      qbv[s] = as_bf16x8(v);
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qbv[s], sacc, 0, 0, 0);
+
+    // sacc[i] = score(key slot 4*gq + i, head n), already scaled by scale*log2(e).
+    if (w.n_valid < BS) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * gq + i >= w.n_valid) sacc[i] = -INFINITY;
+    }
+    float bm = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    const float mnew = fmaxf(mrun, bm);
+    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sacc[i] - mnew);
+    lrun = lrun * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    mrun = mnew;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) oacc[j] *= alpha;
+
+    uint2 pb;
+    pb.x = pack_bf16x2(p[0], p[1]);
+    pb.y = pack_bf16x2(p[2], p[3]);
+    if (w.n_valid < BS) {
+      // Unused slots may hold anything (even NaN): zero their V entries.
+      const int k0 = 4 * gq;
+      const uint32_t m0 = (k0 + 0 < w.n_valid ? 0x0000FFFFu : 0u) | (k0 + 1 < w.n_valid ? 0xFFFF0000u : 0u);
+      const uint32_t m1 = (k0 + 2 < w.n_valid ? 0x0000FFFFu : 0u) | (k0 + 3 < w.n_valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        vr[j].x &= m0;
+        vr[j].y &= m1;
+      }
+    }
+    const i16x4 pbv = as_i16x4(pb);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(vr[j]), pbv, oacc[j], 0, 0, 0);
+  }
+
+  // Wave state -> LDS: lane (n, gq) holds O^T[16j + 4gq + i][head n].
+  lrun += __shfl_xor(lrun, 16, 64);
+  lrun += __shfl_xor(lrun, 32, 64);
+  if (n < G) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mo_lds[wave][n][16 * j + 4 * gq + i] = oacc[j][i];
+    if (gq == 0) {
+      mm_lds[wave][n] = mrun;
+      ml_lds[wave][n] = lrun;
+    }
+  }
+  __syncthreads();
+
+  // Merge the four waves and write the output (or this group's partial).
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int h2 = idx / D;
+    const int d = idx - h2 * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < WAVES; ++wv) M = fmaxf(M, mm_lds[wv][h2]);
+    float O = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int wv = 0; wv < WAVES; ++wv) {
+        const float f = __builtin_amdgcn_exp2f(mm_lds[wv][h2] - M);
+        O += f * mo_lds[wv][h2][d];
+        L += f * ml_lds[wv][h2];
+      }
+    }
+    const int h = g * G + h2;
+    if (groups == 1) {
+      const float inv = L > 0.f ? 1.0f / L : 0.f;
+      out[(static_cast<size_t>(r) * Hq + h) * D + d] = f32_to_bf16(O * inv);
+      if (lse != nullptr && d == 0)
+        lse[static_cast<size_t>(r) * Hq + h] = L > 0.f ? (M + __log2f(L)) * LN2 : -INFINITY;
+    } else {
+      const size_t slot = (static_cast<size_t>(r) * Hq + h) * groups + sg;
+      part_o[slot * D + d] = O;
+      if (d == 0) {
+        part_ml[slot * 2] = M;
+        part_ml[slot * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// Merge split-group partials: one wave per (request, query head).
+__global__ __launch_bounds__(64) void decode_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int groups, int Hq,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const size_t rh = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* ml = part_ml + rh * groups * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < groups; ++s) M = fmaxf(M, ml[2 * s]);
+  float o0 = 0.f, o1 = 0.f, L = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < groups; ++s) {
+      const float ms = ml[2 * s];
+      if (ms == -INFINITY) continue;
+      const float f = __builtin_amdgcn_exp2f(ms - M);
+      const float2 o = *reinterpret_cast<const float2*>(part_o + (rh * groups + s) * D + 2 * lane);
+      o0 += f * o.x;
+      o1 += f * o.y;
+      L += f * ml[2 * s + 1];
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  *reinterpret_cast<uint32_t*>(out + rh * D + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
+  if (lse != nullptr && lane == 0) lse[rh] = L > 0.f ? (M + __log2f(L)) * LN2 : -INFINITY;
+}
+
+template <int G>
+hipError_t launch_g(const AttnArgs& a, const DecodeSplit& s, void* ws, hipStream_t stream) {
+  const int npairs = a.batch * a.num_kv_heads;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (s.groups > 1) {
+    part_o = static_cast<float*>(ws);
+    part_ml = part_o + static_cast<size_t>(a.batch) * a.num_q_heads * s.groups * D;
+  }
+  const float qscale = a.scale * LOG2E;
+  hipLaunchKernelGGL(decode_bf16_kernel<G>, dim3(npairs * s.groups), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
+                     static_cast<const uint16_t*>(a.v_pool), a.words, a.req_blk_start, a.q_pos,
+                     a.cos_sin, a.num_kv_heads, npairs, s.groups, s.group_blocks, qscale, part_o,
+                     part_ml, static_cast<uint16_t*>(a.out), a.lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || s.groups == 1) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.batch * a.num_q_heads), dim3(64), 0, stream,
+                     part_o, part_ml, s.groups, a.num_q_heads, static_cast<uint16_t*>(a.out),
+                     a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+DecodeSplit choose_decode_split(int batch, int num_kv_heads, int max_blocks_per_req,
+                                int split_blocks, int target_workgroups) {
+  DecodeSplit s;
+  const int maxb = max_blocks_per_req > 0 ? max_blocks_per_req : 1;
+  if (split_blocks > 0) {
+    s.group_blocks = split_blocks;
+  } else {
+    const int target = target_workgroups > 0 ? target_workgroups : 1024;
+    const long pairs = static_cast<long>(batch) * num_kv_heads;
+    long want = (target + pairs - 1) / pairs;  // groups per pair to fill the chip
+    // keep at least 8 blocks per wave (32 per 4-wave group)
+    const long cap = (maxb + 31) / 32;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    s.group_blocks = static_cast<int>((maxb + want - 1) / want);
+  }
+  s.groups = (maxb + s.group_blocks - 1) / s.group_blocks;
+  return s;
+}
+
+size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, const DecodeSplit& s) {
+  if (s.groups <= 1) return 0;
+  return static_cast<size_t>(batch) * num_q_heads * s.groups * (head_dim + 2) * sizeof(float);
+}
+
+hipError_t launch_decode_bf16(const AttnArgs& a, const DecodeSplit& s, void* workspace,
+                              hipStream_t stream) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_g<1>(a, s, workspace, stream);
+    case 2: return launch_g<2>(a, s, workspace, stream);
+    case 4: return launch_g<4>(a, s, workspace, stream);
+    case 8: return launch_g<8>(a, s, workspace, stream);
+    case 16: return launch_g<16>(a, s, workspace, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace lazyattn

@@ -1,0 +1,54 @@
+// Internal launch interface between the C-ABI host layer and the HIP kernels.
+// Every launcher enqueues on `stream` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lazyattn {
+
+// Decode work decomposition shared by the workspace query and the launcher:
+// each (request, kv head) pair is cut into `groups` split groups of
+// `group_blocks` consecutive table rows; a split group is one 4-wave workgroup.
+struct DecodeSplit {
+  int groups;        // split groups per (request, kv head)
+  int group_blocks;  // table rows per split group
+};
+
+DecodeSplit choose_decode_split(int batch, int num_kv_heads, int max_blocks_per_req,
+                                int split_blocks, int target_workgroups);
+
+size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, const DecodeSplit& s);
+
+struct AttnArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const uint64_t* words;
+  const int32_t* req_blk_start;
+  const int32_t* cu_q;   // prefill only (nullptr for decode)
+  const int32_t* q_pos;  // decode: m per request; prefill: first new-token position
+  const float* cos_sin;
+  void* out;
+  float* lse;
+  int batch;
+  int num_q_heads;
+  int num_kv_heads;
+  int head_dim;
+  int block_size;
+  int max_q_per_req;   // prefill
+  int max_blocks_per_req;
+  float scale;
+};
+
+// fp32 test-mode kernels (decode and prefill share one kernel).
+hipError_t launch_attn_f32(const AttnArgs& a, bool prefill, hipStream_t stream);
+
+// bf16 split-KV decode (+ cross-split combine when groups > 1).
+hipError_t launch_decode_bf16(const AttnArgs& a, const DecodeSplit& s, void* workspace,
+                              hipStream_t stream);
+
+// bf16 MFMA prefill.
+hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace lazyattn

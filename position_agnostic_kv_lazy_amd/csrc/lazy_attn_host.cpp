@@ -1,0 +1,378 @@
+// Host side of the C ABI declared in include/lazy_attn.h: argument checks,
+// table packing and validation, the cos/sin table, and kernel dispatch.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "lazy_attn.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+la_status fail(la_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+la_status ok() {
+  g_last_error.clear();
+  return LA_OK;
+}
+
+la_status hip_fail(hipError_t e, const char* what) {
+  return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kBf16HeadDim = 128;
+constexpr int kBf16BlockSize = 16;
+
+bool group_supported_bf16(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+// Scalar checks common to every entry point taking la_params.
+la_status check_params(const la_params* p) {
+  if (p == nullptr) return fail(LA_ERR_INVALID_ARG, "params is NULL");
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0)
+    return fail(LA_ERR_INVALID_ARG, "head counts must be positive (Hq=%d, Hkv=%d)",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(LA_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->num_blocks <= 0 || p->num_blocks > LA_MAX_BLOCK_ID)
+    return fail(LA_ERR_INVALID_ARG, "num_blocks %lld outside [1, 2^32]",
+                static_cast<long long>(p->num_blocks));
+  if (p->block_size <= 0 || p->block_size > 128)
+    return fail(LA_ERR_INVALID_ARG, "block_size %d outside [1, 128]", p->block_size);
+  if (p->max_pos <= 0 || p->max_pos > LA_MAX_POSITION)
+    return fail(LA_ERR_INVALID_ARG, "max_pos %d outside [1, 2^24]", p->max_pos);
+  if (!std::isfinite(p->scale)) return fail(LA_ERR_INVALID_ARG, "scale is not finite");
+  if (p->split_blocks < 0 || p->target_workgroups < 0)
+    return fail(LA_ERR_INVALID_ARG, "split_blocks / target_workgroups must be >= 0");
+  for (int i = 0; i < 5; ++i)
+    if (p->reserved[i] != 0) return fail(LA_ERR_INVALID_ARG, "reserved fields must be zero");
+  if (p->dtype == LA_FP32) {
+    if (p->head_dim != 64 && p->head_dim != 128)
+      return fail(LA_ERR_UNSUPPORTED, "fp32 mode supports head_dim 64 or 128, got %d",
+                  p->head_dim);
+  } else if (p->dtype == LA_BF16) {
+    if (p->head_dim != kBf16HeadDim)
+      return fail(LA_ERR_UNSUPPORTED, "bf16 kernels are built for head_dim 128, got %d",
+                  p->head_dim);
+    if (p->block_size != kBf16BlockSize)
+      return fail(LA_ERR_UNSUPPORTED, "bf16 kernels are built for block_size 16, got %d",
+                  p->block_size);
+    if (!group_supported_bf16(p->num_q_heads / p->num_kv_heads))
+      return fail(LA_ERR_UNSUPPORTED, "bf16 kernels support group sizes 1,2,4,8,16, got %d",
+                  p->num_q_heads / p->num_kv_heads);
+    if (p->max_pos < kBf16BlockSize)
+      return fail(LA_ERR_INVALID_ARG, "bf16 decode needs max_pos >= block_size (%d)",
+                  kBf16BlockSize);
+  } else {
+    return fail(LA_ERR_UNSUPPORTED, "unknown dtype %d", p->dtype);
+  }
+  return LA_OK;
+}
+
+uint64_t pack_word(int64_t block_id, int64_t pos0, int n_valid, bool causal) {
+  return static_cast<uint64_t>(block_id) | (static_cast<uint64_t>(pos0) << 32) |
+         (static_cast<uint64_t>(n_valid - 1) << 56) | (causal ? (1ull << 63) : 0ull);
+}
+
+lazyattn::AttnArgs make_args(const la_params* p, const void* q, const void* k_pool,
+                             const void* v_pool, const uint64_t* words,
+                             const int32_t* req_blk_start, const int32_t* cu_q,
+                             const int32_t* q_pos, const float* cos_sin, int batch,
+                             int max_q, int max_blocks, void* out, float* lse) {
+  lazyattn::AttnArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.words = words;
+  a.req_blk_start = req_blk_start;
+  a.cu_q = cu_q;
+  a.q_pos = q_pos;
+  a.cos_sin = cos_sin;
+  a.out = out;
+  a.lse = lse;
+  a.batch = batch;
+  a.num_q_heads = p->num_q_heads;
+  a.num_kv_heads = p->num_kv_heads;
+  a.head_dim = p->head_dim;
+  a.block_size = p->block_size;
+  a.max_q_per_req = max_q;
+  a.max_blocks_per_req = max_blocks;
+  a.scale = p->scale;
+  return a;
+}
+
+// Copy n elements to the host whether src is host or device memory.
+template <typename T>
+la_status fetch(const T* src, size_t n, std::vector<T>& dst) {
+  dst.resize(n);
+  if (n == 0) return LA_OK;
+  hipPointerAttribute_t attr;
+  bool device = false;
+  if (hipPointerGetAttributes(&attr, src) == hipSuccess) {
+    device = attr.type == hipMemoryTypeDevice;
+  } else {
+    (void)hipGetLastError();  // unregistered host pointer: clear the sticky error
+  }
+  if (!device) {
+    std::memcpy(dst.data(), src, n * sizeof(T));
+    return LA_OK;
+  }
+  hipError_t e = hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy (validate_table)");
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+LA_API const char* lazy_attn_status_string(la_status s) {
+  switch (s) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+    case LA_ERR_WORKSPACE_TOO_SMALL: return "LA_ERR_WORKSPACE_TOO_SMALL";
+    case LA_ERR_HIP: return "LA_ERR_HIP";
+  }
+  return "LA_ERR_UNKNOWN";
+}
+
+LA_API const char* lazy_attn_last_error(void) { return g_last_error.c_str(); }
+
+LA_API la_status lazy_attn_rope_table(double base, int32_t head_dim, int32_t rows, float* out) {
+  try {
+    if (out == nullptr) return fail(LA_ERR_INVALID_ARG, "out is NULL");
+    if (!(base > 1.0) || !std::isfinite(base))
+      return fail(LA_ERR_INVALID_ARG, "RoPE base must be finite and > 1");
+    if (head_dim < 2 || head_dim > 1024 || head_dim % 2 != 0)
+      return fail(LA_ERR_INVALID_ARG, "head_dim must be even in [2, 1024], got %d", head_dim);
+    if (rows < 1 || rows > LA_MAX_POSITION)
+      return fail(LA_ERR_INVALID_ARG, "rows must be in [1, 2^24], got %d", rows);
+    const int half = head_dim / 2;
+    std::vector<double> theta(half);
+    for (int i = 0; i < half; ++i)
+      theta[i] = std::pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(head_dim));
+    for (int64_t pos = 0; pos < rows; ++pos) {
+      float* row = out + pos * head_dim;
+      for (int i = 0; i < half; ++i) {
+        const double ang = static_cast<double>(pos) * theta[i];
+        row[i] = static_cast<float>(std::cos(ang));
+        row[half + i] = static_cast<float>(std::sin(ang));
+      }
+    }
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_INVALID_ARG, "unexpected exception in lazy_attn_rope_table");
+  }
+}
+
+LA_API la_status lazy_attn_pack_segments(const la_params* p, int32_t batch,
+                                         const int64_t* req_seg_start, const int64_t* seg_start,
+                                         const int64_t* seg_len, const uint8_t* seg_is_new,
+                                         const int64_t* seg_blk_start, const int64_t* seg_blocks,
+                                         uint64_t* blk_words, int64_t capacity,
+                                         int32_t* req_blk_start, int32_t* max_blocks_per_req) {
+  try {
+    la_status st = check_params(p);
+    if (st != LA_OK) return st;
+    if (batch < 1) return fail(LA_ERR_INVALID_ARG, "batch must be >= 1");
+    if (!req_seg_start || !seg_start || !seg_len || !seg_is_new || !seg_blk_start || !seg_blocks ||
+        !blk_words || !req_blk_start)
+      return fail(LA_ERR_INVALID_ARG, "NULL array passed to lazy_attn_pack_segments");
+    const int64_t BS = p->block_size;
+    const int64_t pos_limit = p->max_pos;
+    int64_t w = 0;
+    int32_t maxb = 0;
+    if (req_seg_start[0] != 0) return fail(LA_ERR_INVALID_ARG, "req_seg_start[0] must be 0");
+    for (int r = 0; r < batch; ++r) {
+      const int64_t s0 = req_seg_start[r], s1 = req_seg_start[r + 1];
+      if (s1 < s0) return fail(LA_ERR_INVALID_ARG, "req_seg_start decreases at request %d", r);
+      req_blk_start[r] = static_cast<int32_t>(w);
+      int64_t tokens = 0;
+      for (int64_t s = s0; s < s1; ++s) {
+        const int64_t n = seg_len[s], start = seg_start[s];
+        if (n < 1) return fail(LA_ERR_INVALID_ARG, "segment %lld has %lld tokens", (long long)s, (long long)n);
+        if (start < 0 || start + n - 1 >= pos_limit)
+          return fail(LA_ERR_INVALID_ARG,
+                      "segment %lld covers positions [%lld, %lld], outside [0, max_pos=%lld)",
+                      (long long)s, (long long)start, (long long)(start + n - 1), (long long)pos_limit);
+        const int64_t nb = (n + BS - 1) / BS;
+        if (seg_blk_start[s + 1] - seg_blk_start[s] != nb)
+          return fail(LA_ERR_INVALID_ARG, "segment %lld of %lld tokens lists %lld blocks, needs %lld",
+                      (long long)s, (long long)n, (long long)(seg_blk_start[s + 1] - seg_blk_start[s]),
+                      (long long)nb);
+        for (int64_t k = 0; k < nb; ++k) {
+          const int64_t id = seg_blocks[seg_blk_start[s] + k];
+          if (id < 0 || id >= p->num_blocks)
+            return fail(LA_ERR_INVALID_ARG, "block id %lld outside [0, num_blocks=%lld)",
+                        (long long)id, (long long)p->num_blocks);
+          if (w >= capacity)
+            return fail(LA_ERR_INVALID_ARG, "blk_words capacity %lld too small", (long long)capacity);
+          const int nv = static_cast<int>(k + 1 < nb ? BS : n - k * BS);
+          blk_words[w++] = pack_word(id, start + k * BS, nv, seg_is_new[s] != 0);
+        }
+        tokens += n;
+      }
+      if (tokens == 0) return fail(LA_ERR_INVALID_ARG, "request %d has no keys", r);
+      const int64_t nbr = w - req_blk_start[r];
+      if (nbr > maxb) maxb = static_cast<int32_t>(nbr);
+      if (w > INT32_MAX) return fail(LA_ERR_INVALID_ARG, "more than 2^31 table rows");
+    }
+    req_blk_start[batch] = static_cast<int32_t>(w);
+    if (max_blocks_per_req) *max_blocks_per_req = maxb;
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_INVALID_ARG, "unexpected exception in lazy_attn_pack_segments");
+  }
+}
+
+LA_API la_status lazy_attn_validate_table(const la_params* p, int32_t batch,
+                                          const uint64_t* blk_words, const int32_t* req_blk_start,
+                                          const int32_t* q_pos, const int32_t* cu_q) {
+  try {
+    la_status st = check_params(p);
+    if (st != LA_OK) return st;
+    if (batch < 1) return fail(LA_ERR_INVALID_ARG, "batch must be >= 1");
+    if (!blk_words || !req_blk_start || !q_pos)
+      return fail(LA_ERR_INVALID_ARG, "NULL array passed to lazy_attn_validate_table");
+    std::vector<int32_t> rbs, qp, cq;
+    if ((st = fetch(req_blk_start, batch + 1, rbs)) != LA_OK) return st;
+    if ((st = fetch(q_pos, batch, qp)) != LA_OK) return st;
+    if (cu_q && (st = fetch(cu_q, batch + 1, cq)) != LA_OK) return st;
+    if (rbs[0] < 0) return fail(LA_ERR_INVALID_ARG, "req_blk_start[0] < 0");
+    for (int r = 0; r < batch; ++r)
+      if (rbs[r + 1] <= rbs[r]) return fail(LA_ERR_INVALID_ARG, "request %d has no blocks", r);
+    std::vector<uint64_t> words;
+    if ((st = fetch(blk_words, static_cast<size_t>(rbs[batch]), words)) != LA_OK) return st;
+    for (int r = 0; r < batch; ++r) {
+      const int64_t m0 = qp[r];
+      const int64_t nq = cu_q ? static_cast<int64_t>(cq[r + 1]) - cq[r] : 1;
+      if (nq < 1) return fail(LA_ERR_INVALID_ARG, "request %d has %lld query rows", r, (long long)nq);
+      if (m0 < 0 || m0 + nq - 1 >= p->max_pos)
+        return fail(LA_ERR_INVALID_ARG, "request %d query positions [%lld, %lld] outside max_pos %d",
+                    r, (long long)m0, (long long)(m0 + nq - 1), p->max_pos);
+      int64_t min_causal = INT64_MAX;
+      bool has_cached = false;
+      for (int32_t b = rbs[r]; b < rbs[r + 1]; ++b) {
+        const uint64_t wd = words[b - rbs[0]];
+        const int64_t id = static_cast<int64_t>(wd & 0xFFFFFFFFull);
+        const int64_t pos0 = static_cast<int64_t>((wd >> 32) & 0xFFFFFFull);
+        const int nv = static_cast<int>((wd >> 56) & 0x7Full) + 1;
+        const bool causal = (wd >> 63) != 0;
+        if (id >= p->num_blocks)
+          return fail(LA_ERR_INVALID_ARG, "row %d: block id %lld >= num_blocks", b, (long long)id);
+        if (nv > p->block_size)
+          return fail(LA_ERR_INVALID_ARG, "row %d: n_valid %d > block_size", b, nv);
+        if (pos0 + nv - 1 >= p->max_pos)
+          return fail(LA_ERR_INVALID_ARG, "row %d: position %lld >= max_pos %d", b,
+                      (long long)(pos0 + nv - 1), p->max_pos);
+        if (causal && cu_q) {
+          if (pos0 < min_causal) min_causal = pos0;
+        } else {
+          has_cached = true;
+        }
+      }
+      if (cu_q && !has_cached && min_causal > m0)
+        return fail(LA_ERR_INVALID_ARG, "request %d: first query row sees no key", r);
+    }
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_INVALID_ARG, "unexpected exception in lazy_attn_validate_table");
+  }
+}
+
+LA_API la_status lazy_attn_decode_workspace_size(const la_params* p, int32_t batch,
+                                                 int32_t max_blocks_per_req, size_t* bytes) {
+  la_status st = check_params(p);
+  if (st != LA_OK) return st;
+  if (bytes == nullptr) return fail(LA_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 1 || max_blocks_per_req < 1)
+    return fail(LA_ERR_INVALID_ARG, "batch and max_blocks_per_req must be >= 1");
+  if (p->dtype == LA_FP32) {
+    *bytes = 0;
+    return ok();
+  }
+  const lazyattn::DecodeSplit s = lazyattn::choose_decode_split(
+      batch, p->num_kv_heads, max_blocks_per_req, p->split_blocks, p->target_workgroups);
+  *bytes = lazyattn::decode_workspace_bytes(batch, p->num_q_heads, p->head_dim, s);
+  return ok();
+}
+
+LA_API la_status lazy_attn_decode(const la_params* p, const void* q, const void* k_pool,
+                                  const void* v_pool, const uint64_t* blk_words,
+                                  const int32_t* req_blk_start, const int32_t* q_pos,
+                                  const float* cos_sin, int32_t batch, int32_t max_blocks_per_req,
+                                  void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  try {
+    la_status st = check_params(p);
+    if (st != LA_OK) return st;
+    if (!q || !k_pool || !v_pool || !blk_words || !req_blk_start || !q_pos || !cos_sin || !out)
+      return fail(LA_ERR_INVALID_ARG, "NULL device pointer passed to lazy_attn_decode");
+    if (batch < 1 || max_blocks_per_req < 1)
+      return fail(LA_ERR_INVALID_ARG, "batch and max_blocks_per_req must be >= 1");
+    const lazyattn::AttnArgs a = make_args(p, q, k_pool, v_pool, blk_words, req_blk_start, nullptr,
+                                           q_pos, cos_sin, batch, 1, max_blocks_per_req, out, lse);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (p->dtype == LA_FP32) {
+      e = lazyattn::launch_attn_f32(a, false, s);
+    } else {
+      const lazyattn::DecodeSplit sp = lazyattn::choose_decode_split(
+          batch, p->num_kv_heads, max_blocks_per_req, p->split_blocks, p->target_workgroups);
+      const size_t need = lazyattn::decode_workspace_bytes(batch, p->num_q_heads, p->head_dim, sp);
+      if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(LA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need,
+                    workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+      e = lazyattn::launch_decode_bf16(a, sp, workspace, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "lazy_attn_decode launch");
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_HIP, "unexpected exception in lazy_attn_decode");
+  }
+}
+
+LA_API la_status lazy_attn_prefill(const la_params* p, const void* q, const void* k_pool,
+                                   const void* v_pool, const uint64_t* blk_words,
+                                   const int32_t* req_blk_start, const int32_t* cu_q,
+                                   const int32_t* q_pos0, const float* cos_sin, int32_t batch,
+                                   int32_t max_q_per_req, void* out, float* lse, void* stream) {
+  try {
+    la_status st = check_params(p);
+    if (st != LA_OK) return st;
+    if (!q || !k_pool || !v_pool || !blk_words || !req_blk_start || !cu_q || !q_pos0 || !cos_sin ||
+        !out)
+      return fail(LA_ERR_INVALID_ARG, "NULL device pointer passed to lazy_attn_prefill");
+    if (batch < 1 || max_q_per_req < 1)
+      return fail(LA_ERR_INVALID_ARG, "batch and max_q_per_req must be >= 1");
+    if (max_q_per_req > 65535 && p->dtype == LA_FP32)
+      return fail(LA_ERR_UNSUPPORTED, "fp32 prefill supports at most 65535 rows per request");
+    const lazyattn::AttnArgs a = make_args(p, q, k_pool, v_pool, blk_words, req_blk_start, cu_q,
+                                           q_pos0, cos_sin, batch, max_q_per_req, 0, out, lse);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = p->dtype == LA_FP32 ? lazyattn::launch_attn_f32(a, true, s)
+                                             : lazyattn::launch_prefill_bf16(a, s);
+    if (e != hipSuccess) return hip_fail(e, "lazy_attn_prefill launch");
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_HIP, "unexpected exception in lazy_attn_prefill");
+  }
+}
+
+}  // extern "C"

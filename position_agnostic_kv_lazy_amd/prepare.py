@@ -1,0 +1,119 @@
+"""Stage host-side inputs in device memory in the layouts the C ABI expects.
+
+Input preparation only (outside any timed region): it converts a host pool to
+the device layout (V tiles dim-major), builds the cos/sin table and the packed
+block table through the library's own host entry points, and allocates
+outputs and the decode workspace.  All attention arithmetic happens in the
+HIP kernels behind lazy_attn_decode / lazy_attn_prefill.
+
+A "batch description" is any object with the attributes used below
+(kind, dtype, num_q_heads, num_kv_heads, head_dim, block_size, rope_base,
+scale, requests, q, q_pos, cu_q, table_rows(), batch); the pools are passed
+separately so several batches can share one device pool.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def _to_device_bits(a: np.ndarray, device) -> torch.Tensor:
+    """uint16 (bf16 bits) -> int16 tensor with the same bits; float32 as is."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def upload_pool(k_pool: np.ndarray, v_pool: np.ndarray, device="cuda", chunk_blocks=8192):
+    """Copy a logical [nb, Hkv, BS, D] pool pair to the device layouts.
+
+    K keeps [nb, Hkv, BS, D]; V becomes [nb, Hkv, D, BS] (dim-major tiles).
+    Large pools are streamed in chunks to bound host and device staging.
+    """
+    nb = k_pool.shape[0]
+    k_dev = _to_device_bits(k_pool, device)
+    shape_t = (nb, v_pool.shape[1], v_pool.shape[3], v_pool.shape[2])
+    dt = torch.int16 if v_pool.dtype == np.uint16 else torch.float32
+    v_dev = torch.empty(shape_t, dtype=dt, device=device)
+    for a in range(0, nb, chunk_blocks):
+        b = min(nb, a + chunk_blocks)
+        v_dev[a:b] = _to_device_bits(v_pool[a:b], device).transpose(-1, -2)
+    return k_dev, v_dev
+
+
+@dataclass
+class DeviceBatch:
+    kind: str
+    params: B.la_params
+    q: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    words: torch.Tensor
+    req_blk_start: torch.Tensor
+    q_pos: torch.Tensor
+    cu_q: Optional[torch.Tensor]
+    cos_sin: torch.Tensor
+    out: torch.Tensor
+    lse: torch.Tensor
+    workspace: Optional[torch.Tensor]
+    batch: int
+    max_blocks: int
+    max_q: int
+    host_words: np.ndarray
+    host_rbs: np.ndarray
+
+    def run(self, stream=None):
+        if self.kind == "decode":
+            B.lazy_attn_decode(self.params, self.q, self.k_pool, self.v_pool, self.words,
+                               self.req_blk_start, self.q_pos, self.cos_sin, self.batch,
+                               self.max_blocks, self.out, self.lse, self.workspace, stream)
+        else:
+            B.lazy_attn_prefill(self.params, self.q, self.k_pool, self.v_pool, self.words,
+                                self.req_blk_start, self.cu_q, self.q_pos, self.cos_sin,
+                                self.batch, self.max_q, self.out, self.lse, stream)
+
+    def out_f32(self) -> np.ndarray:
+        """Output as float32 numpy (bf16 bits widened exactly)."""
+        o = self.out.cpu().numpy()
+        if o.dtype == np.int16:
+            return (o.view(np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+        return o
+
+
+def prepare(w, k_dev: torch.Tensor, v_dev: torch.Tensor, device="cuda", split_blocks: int = 0,
+            target_workgroups: int = 0, max_pos: Optional[int] = None) -> DeviceBatch:
+    """Pack and upload everything lazy_attn_decode/prefill need for batch w."""
+    rows = int(max_pos) if max_pos is not None else int(w.table_rows())
+    params = B.make_params(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                           head_dim=w.head_dim, block_size=w.block_size,
+                           num_blocks=int(k_dev.shape[0]), dtype=w.dtype, scale=w.scale,
+                           max_pos=rows, split_blocks=split_blocks,
+                           target_workgroups=target_workgroups)
+    words, rbs, maxb = B.lazy_attn_pack_segments(params, w.requests)
+    table = B.lazy_attn_rope_table(w.rope_base, w.head_dim, rows)
+    q = _to_device_bits(w.q, device)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=device)
+    q_pos = torch.from_numpy(np.asarray(w.q_pos, dtype=np.int32)).to(device)
+    cu_q = None
+    max_q = 1
+    if w.kind == "prefill":
+        cu = np.asarray(w.cu_q, dtype=np.int32)
+        cu_q = torch.from_numpy(cu).to(device)
+        max_q = int(np.max(np.diff(cu)))
+    ws = None
+    if w.kind == "decode":
+        nbytes = B.lazy_attn_decode_workspace_size(params, w.batch, maxb)
+        if nbytes:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return DeviceBatch(
+        kind=w.kind, params=params, q=q, k_pool=k_dev, v_pool=v_dev,
+        words=torch.from_numpy(words.view(np.int64)).to(device),
+        req_blk_start=torch.from_numpy(rbs).to(device), q_pos=q_pos, cu_q=cu_q,
+        cos_sin=torch.from_numpy(table).to(device), out=out, lse=lse, workspace=ws,
+        batch=w.batch, max_blocks=maxb, max_q=max_q, host_words=words, host_rbs=rbs)

@@ -1,0 +1,205 @@
+"""C-ABI host layer on the CPU: exports, cos/sin table, packing, validation, errors.
+
+No kernel is launched here: every call either is host-only or fails argument
+validation before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import position_agnostic_kv_lazy_amd as la
+from position_agnostic_kv_lazy_amd import binding as B
+from workloads import Segment, make_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lazy_attn.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"LA_API\s+[\w\s\*]+?\b(lazy_attn_\w+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 8, names
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTED) == names
+
+
+def test_status_strings():
+    assert la.lazy_attn_status_string(0) == "LA_OK"
+    assert la.lazy_attn_status_string(3) == "LA_ERR_WORKSPACE_TOO_SMALL"
+    assert la.lazy_attn_status_string(99) == "LA_ERR_UNKNOWN"
+
+
+def test_params_struct_layout():
+    # int32 x4, int64, int32, float, int32 x3, int32[5] -> 64 bytes, int64 at offset 16
+    assert ctypes.sizeof(B.la_params) == 64
+    assert B.la_params.num_blocks.offset == 16
+
+
+def test_rope_table_matches_oracle_definition():
+    from oracle import rope_theta
+    D, rows, base = 128, 70000, 5e5
+    t = la.lazy_attn_rope_table(base, D, rows)
+    th = rope_theta(D, base)
+    for p in (0, 1, 15, 5184, 65535, 69999):
+        ang = p * th
+        np.testing.assert_allclose(t[p, :64], np.cos(ang), atol=6e-8, rtol=0)
+        np.testing.assert_allclose(t[p, 64:], np.sin(ang), atol=6e-8, rtol=0)
+    # float32 rounding of the float64 value: exact to half an ulp
+    ref = np.cos(69999 * th).astype(np.float32)
+    np.testing.assert_array_equal(t[69999, :64], ref)
+
+
+def test_rope_table_errors():
+    with pytest.raises(la.LazyAttnError, match="INVALID_ARG"):
+        la.lazy_attn_rope_table(1.0, 128, 10)
+    with pytest.raises(la.LazyAttnError, match="even"):
+        la.lazy_attn_rope_table(1e4, 127, 10)
+
+
+def _params(**kw):
+    d = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=1000,
+             dtype="bf16", scale=0.088, max_pos=20000)
+    d.update(kw)
+    return la.make_params(**d)
+
+
+def _unpack(words):
+    w = words.astype(np.uint64)
+    return (w & np.uint64(0xFFFFFFFF)).astype(np.int64), \
+        ((w >> np.uint64(32)) & np.uint64(0xFFFFFF)).astype(np.int64), \
+        ((w >> np.uint64(56)) & np.uint64(0x7F)).astype(np.int64) + 1, \
+        (w >> np.uint64(63)).astype(np.int64)
+
+
+def test_pack_segments_round_trip():
+    w = make_config(3, scale_down=4)
+    p = _params(num_blocks=w.num_blocks, max_pos=w.table_rows())
+    words, rbs, maxb = la.lazy_attn_pack_segments(p, w.requests)
+    ids, pos0, nv, causal = _unpack(words)
+    assert rbs[0] == 0 and len(rbs) == w.batch + 1
+    assert maxb == int(np.max(np.diff(rbs)))
+    for r, segs in enumerate(w.requests):
+        row = rbs[r]
+        for s in segs:
+            for k, b in enumerate(s.blocks):
+                assert ids[row] == b and pos0[row] == s.start + 16 * k
+                assert nv[row] == min(16, s.n_tokens - 16 * k)
+                assert causal[row] == int(s.is_new)
+                row += 1
+        assert row == rbs[r + 1]
+
+
+def test_pack_segments_partial_blocks():
+    p = _params(num_blocks=10, max_pos=100)
+    segs = [[Segment(3, 20, np.array([4, 2]), False), Segment(60, 5, np.array([9]), True)]]
+    words, rbs, _ = la.lazy_attn_pack_segments(p, segs)
+    ids, pos0, nv, causal = _unpack(words)
+    assert list(ids) == [4, 2, 9] and list(pos0) == [3, 19, 60]
+    assert list(nv) == [16, 4, 5] and list(causal) == [0, 0, 1]
+
+
+@pytest.mark.parametrize("segs,msg", [
+    ([[Segment(0, 20, np.array([4]), False)]], "needs 2"),
+    ([[Segment(0, 5, np.array([10]), False)]], "block id 10"),
+    ([[Segment(98, 5, np.array([1]), False)]], "max_pos"),
+    ([[Segment(-1, 5, np.array([1]), False)]], "outside"),
+    ([[Segment(0, 0, np.array([], np.int64), False)]], "0 tokens"),
+    ([[]], "no keys"),
+])
+def test_pack_segments_rejects(segs, msg):
+    p = _params(num_blocks=10, max_pos=100)
+    with pytest.raises(la.LazyAttnError, match=msg):
+        la.lazy_attn_pack_segments(p, segs)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(num_kv_heads=5), "INVALID_ARG", "multiple"),
+    (dict(head_dim=64), "UNSUPPORTED", "head_dim 128"),
+    (dict(block_size=32), "UNSUPPORTED", "block_size 16"),
+    (dict(num_q_heads=24), "UNSUPPORTED", "group sizes"),
+    (dict(dtype=7), "UNSUPPORTED", "dtype"),
+    (dict(max_pos=0), "INVALID_ARG", "max_pos"),
+    (dict(num_blocks=0), "INVALID_ARG", "num_blocks"),
+    (dict(scale=float("nan")), "INVALID_ARG", "scale"),
+])
+def test_param_validation(kw, status, msg):
+    p = _params(**kw)
+    with pytest.raises(la.LazyAttnError, match=f"{status}.*{msg}"):
+        la.lazy_attn_decode_workspace_size(p, 4, 10)
+
+
+def test_reserved_fields_must_be_zero():
+    p = _params()
+    p.reserved[2] = 1
+    with pytest.raises(la.LazyAttnError, match="reserved"):
+        la.lazy_attn_decode_workspace_size(p, 4, 10)
+
+
+def test_fp32_mode_allows_head_dim_64():
+    p = _params(dtype="f32", head_dim=64, num_q_heads=1, num_kv_heads=1)
+    assert la.lazy_attn_decode_workspace_size(p, 1, 10) == 0
+
+
+def test_workspace_size_formula():
+    p = _params()
+    # cfg2 shape: 64 requests x 8 kv heads = 512 pairs, 324 blocks each
+    n = la.lazy_attn_decode_workspace_size(p, 64, 324)
+    groups = 2  # ceil(1024 / 512) groups per pair
+    assert n == 64 * 32 * groups * 130 * 4
+    # enough pairs to fill the target: one group, no workspace, no combine
+    assert la.lazy_attn_decode_workspace_size(p, 256, 324) == 0
+    # explicit split size
+    p2 = _params(split_blocks=100)
+    assert la.lazy_attn_decode_workspace_size(p2, 64, 324) == 64 * 32 * 4 * 130 * 4
+    # long context: 16 x 8 pairs, 4096 blocks -> 8 groups
+    assert la.lazy_attn_decode_workspace_size(p, 16, 4096) == 16 * 32 * 8 * 130 * 4
+
+
+def test_validate_table_host_arrays():
+    w = make_config(2, scale_down=8)
+    p = _params(num_blocks=w.num_blocks, max_pos=w.table_rows())
+    words, rbs, _ = la.lazy_attn_pack_segments(p, w.requests)
+    qpos = w.q_pos.astype(np.int32)
+    la.lazy_attn_validate_table(p, w.batch, words, rbs, qpos)
+    bad = qpos.copy()
+    bad[1] = w.table_rows()
+    with pytest.raises(la.LazyAttnError, match="query positions"):
+        la.lazy_attn_validate_table(p, w.batch, words, rbs, bad)
+    p_small = _params(num_blocks=10, max_pos=w.table_rows())
+    with pytest.raises(la.LazyAttnError, match="num_blocks"):
+        la.lazy_attn_validate_table(p_small, w.batch, words, rbs, qpos)
+
+
+def test_validate_table_prefill_needs_visible_key():
+    p = _params(num_blocks=10, max_pos=100)
+    segs = [[Segment(50, 5, np.array([1]), True)]]
+    words, rbs, _ = la.lazy_attn_pack_segments(p, segs)
+    cu = np.array([0, 3], np.int32)
+    la.lazy_attn_validate_table(p, 1, words, rbs, np.array([50], np.int32), cu)
+    with pytest.raises(la.LazyAttnError, match="sees no key"):
+        la.lazy_attn_validate_table(p, 1, words, rbs, np.array([40], np.int32), cu)
+
+
+def test_null_pointers_rejected_before_launch():
+    p = _params()
+    with pytest.raises(la.LazyAttnError, match="NULL"):
+        la.lazy_attn_decode(p, None, None, None, None, None, None, None, 1, 1, None)
+    with pytest.raises(la.LazyAttnError, match="NULL"):
+        la.lazy_attn_prefill(p, None, None, None, None, None, None, None, None, 1, 1, None)
+
+
+def test_workspace_too_small_rejected_before_launch():
+    p = _params()
+    fake = 1 << 40  # never dereferenced: the size check fails first
+    with pytest.raises(la.LazyAttnError, match="WORKSPACE_TOO_SMALL"):
+        la.lazy_attn_decode(p, fake, fake, fake, fake, fake, fake, fake, 64, 324, fake,
+                            None, None, None)
