@@ -142,23 +142,122 @@ def roofline_mfma(flops, ms, kind, workload):
 
 
 def cpu_baseline(w, budget_s=12.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the headline workload."""
+    """The fp64 oracle, as it stands, on a bounded sample of the headline workload.
+
+    Requests (decode) or 16-row slices of new tokens (prefill) are run in turn
+    until about budget_s seconds of single-threaded CPU work are done.
+    """
     from threadpoolctl import threadpool_limits
 
-    from oracle import run_decode
+    from oracle import run_decode, run_prefill
     t0 = time.perf_counter()
-    done = 0
-    nbytes = 0
-    keys = w.keys_per_request()
+    work = 0
+    units = 0
     with threadpool_limits(limits=1):
-        while done < w.batch and (time.perf_counter() - t0 < budget_s or done < 2):
-            run_decode(w, requests=[done])
-            nbytes += int(keys[done]) * w.num_kv_heads * w.head_dim * 2 * 2
-            done += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {w.batch} requests of the headline decode batch, fp64 NumPy, "
-                      f"BLAS limited to 1 thread, {dt:.1f} s"}
+        if w.kind == "decode":
+            keys = w.keys_per_request()
+            while time.perf_counter() - t0 < budget_s or units < 2:
+                r = units % w.batch
+                run_decode(w, requests=[r])
+                work += int(keys[r]) * w.num_kv_heads * w.head_dim * 2 * 2
+                units += 1
+            dt = time.perf_counter() - t0
+            return {"value": round(work / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                    "kind": "oracle",
+                    "sample": f"{units} decode requests (cycling over the {w.batch}-request "
+                              f"batch), fp64 NumPy, BLAS limited to 1 thread, {dt:.1f} s"}
+        cached = w.keys_per_request() - np.array([w.q_len(r) for r in range(w.batch)])
+        while time.perf_counter() - t0 < budget_s or units < 1:
+            r = units % w.batch
+            rows = np.arange(16 * (units // w.batch) % w.q_len(r), w.q_len(r))[:16]
+            run_prefill(w, requests=[r], rows={r: rows})
+            work += int(sum(4 * w.head_dim * w.num_q_heads * (int(cached[r]) + int(j) + 1)
+                            for j in rows))
+            units += 1
+        dt = time.perf_counter() - t0
+        return {"value": round(work / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                "kind": "oracle",
+                "sample": f"{units} slices of 16 new-token rows, fp64 NumPy, BLAS limited to "
+                          f"1 thread, {dt:.1f} s"}
+
+
+def _clean(res):
+    return {kk: (round(vv, 5) if isinstance(vv, float) else vv)
+            for kk, vv in res.items() if not kk.startswith("_")}
+
+
+def _extra_prefill(stream, steps):
+    from position_agnostic_kv_lazy_amd.prepare import upload_pool
+    from workloads import make_config
+    try:
+        log("prefill (Llama-3-8B shapes, 8 requests x 10240 cached + 512 new)")
+        w3 = make_config(3)
+        k3, v3 = upload_pool(w3.k_pool, w3.v_pool)
+        r3 = run_prefill_workload(w3, k3, v3, stream, steps, 3)
+        out = _clean(r3)
+        out["roofline"] = roofline_mfma(r3["flops"], r3["event_ms_mean"], "prefill", w3.name)
+        return {w3.name: out}
+    except Exception as e:  # reported, never hidden
+        return {"llama3_8b_prefill": {"error": repr(e)}}
+
+
+def _extra_long_decode(stream, steps):
+    from position_agnostic_kv_lazy_amd.prepare import upload_pool
+    from workloads import make_config
+    log("long-context decode (16 requests x 64K keys)")
+    w4 = make_config(4)
+    k4, v4 = upload_pool(w4.k_pool, w4.v_pool)
+    r4 = run_decode_workload(w4, k4, v4, stream, steps, 3)
+    out = _clean(r4)
+    out["roofline"] = roofline_hbm(r4["logical_kv_bytes"], r4["event_ms_mean"], "decode", w4.name)
+    return {w4.name: out}
+
+
+def _extra_mixed(stream, steps):
+    """Config 5: one decode launch and one prefill launch on one shared pool."""
+    import torch
+
+    from position_agnostic_kv_lazy_amd.prepare import prepare, upload_pool
+    from workloads import make_config
+    try:
+        log("mixed step: 128 decode + 4 prefill requests on one pool")
+        m5 = make_config(5)
+        k5, v5 = upload_pool(m5.prefill.k_pool, m5.prefill.v_pool)
+        dd = prepare(m5.decode, k5, v5)
+        dp = prepare(m5.prefill, k5, v5)
+        s2 = torch.cuda.Stream()
+
+        def pair_two_streams():
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            s2.wait_event(ev)
+            dp.run(s2)
+            dd.run(stream)
+            e2 = torch.cuda.Event()
+            e2.record(s2)
+            stream.wait_event(e2)
+
+        def pair_serial():
+            dp.run(stream)
+            dd.run(stream)
+
+        _, p2, _, _ = time_launches(pair_two_streams, steps, 3, stream)
+        _, p1, _, _ = time_launches(pair_serial, steps, 3, stream)
+        _, dm, _, _ = time_launches(lambda: dd.run(stream), steps, 3, stream)
+        _, fm, _, _ = time_launches(lambda: dp.run(stream), steps, 3, stream)
+        nb = m5.decode.logical_kv_bytes()
+        fl = m5.prefill.prefill_flops()
+        return {"mixed_step": {
+            "pair_serial_event_ms_mean": round(p1, 5),
+            "pair_two_streams_event_ms_mean": round(p2, 5),
+            "decode_event_ms_mean": round(dm, 5),
+            "prefill_event_ms_mean": round(fm, 5),
+            "decode_gbs_logical": round(nb / (dm * 1e-3) / 1e9, 1),
+            "prefill_tflops": round(fl / (fm * 1e-3) / 1e12, 1),
+            "decode_logical_kv_bytes": nb, "prefill_flops": fl,
+        }}
+    except Exception as e:
+        return {"mixed_step": {"error": repr(e)}}
 
 
 def main():
@@ -166,7 +265,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 4])
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4],
+                    help="headline workload: 2 decode (default), 3 prefill, 4 long decode")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--split-blocks", type=int, default=0)
@@ -197,15 +297,30 @@ def main():
     log(f"generating config {args.config}")
     w = make_config(args.config)
     k, v = upload_pool(w.k_pool, w.v_pool)
-    log("timing headline decode")
-    main_res = run_decode_workload(w, k, v, stream, args.steps, args.warmup, args.split_blocks)
-    ms = main_res["wall_ms_per_step"]
-    value = main_res["logical_kv_bytes"] / (ms * 1e-3) / 1e9
     wl_name = w.name
+    config = {"workload": wl_name, "batch": w.batch, "q_heads": w.num_q_heads,
+              "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+              "docs": "Zipf document mix, shared physical blocks"}
+    if w.kind == "decode":
+        log("timing headline decode")
+        main_res = run_decode_workload(w, k, v, stream, args.steps, args.warmup, args.split_blocks)
+        ms = main_res["wall_ms_per_step"]
+        value, unit = main_res["logical_kv_bytes"] / (ms * 1e-3) / 1e9, "GB/s"
+        config["keys_per_request"] = int(w.keys_per_request()[0])
+        roof = roofline_hbm(main_res["logical_kv_bytes"], main_res["event_ms_mean"], "decode",
+                            wl_name)
+    else:
+        log("timing headline prefill")
+        main_res = run_prefill_workload(w, k, v, stream, args.steps, args.warmup)
+        ms = main_res["wall_ms_per_step"]
+        value, unit = main_res["flops"] / (ms * 1e-3) / 1e12, "TFLOP/s"
+        config["new_tokens_per_request"] = int(w.q_len(0))
+        config["cached_keys_per_request"] = int(w.keys_per_request()[0] - w.q_len(0))
+        roof = roofline_mfma(main_res["flops"], main_res["event_ms_mean"], "prefill", wl_name)
     result = {
         "metric": METRIC,
         "value": round(value, 1),
-        "unit": "GB/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -215,80 +330,22 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl_name, "batch": w.batch,
-                   "keys_per_request": int(w.keys_per_request()[0]),
-                   "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
-                   "head_dim": w.head_dim, "block_size": w.block_size,
-                   "docs": "Zipf document mix, shared physical blocks"},
-        "roofline": roofline_hbm(main_res["logical_kv_bytes"], main_res["event_ms_mean"],
-                                 "decode", wl_name),
+        "config": config,
+        "roofline": roof,
     }
-    extra = {wl_name: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
-                       for kk, vv in main_res.items() if not kk.startswith("_")}}
-    del main_res
-    del k, v
+    extra = {wl_name: _clean(main_res)}
+    del main_res, k, v
     torch.cuda.empty_cache()
 
     if not args.no_extra:
         steps2 = max(5, args.steps // 2)
-        try:
-            log("prefill (Llama-3-8B shapes, 8 requests x 10240 cached + 512 new)")
-            w3 = make_config(3)
-            k3, v3 = upload_pool(w3.k_pool, w3.v_pool)
-            r3 = run_prefill_workload(w3, k3, v3, stream, steps2, 3)
-            extra[w3.name] = {kk: (round(vv, 5) if isinstance(vv, float) else vv)
-                              for kk, vv in r3.items() if not kk.startswith("_")}
-            extra[w3.name]["roofline"] = roofline_mfma(r3["flops"], r3["event_ms_mean"],
-                                                       "prefill", w3.name)
-            del r3, k3, v3, w3
-        except Exception as e:  # reported, never hidden
-            extra["llama3_8b_prefill"] = {"error": repr(e)}
-        torch.cuda.empty_cache()
-        if args.config != 4:
-            log("long-context decode (16 requests x 64K keys)")
-            w4 = make_config(4)
-            k4, v4 = upload_pool(w4.k_pool, w4.v_pool)
-            r4 = run_decode_workload(w4, k4, v4, stream, steps2, 3)
-            extra[w4.name] = {kk: (round(vv, 5) if isinstance(vv, float) else vv)
-                              for kk, vv in r4.items() if not kk.startswith("_")}
-            extra[w4.name]["roofline"] = roofline_hbm(r4["logical_kv_bytes"],
-                                                      r4["event_ms_mean"], "decode", w4.name)
-            del r4, k4, v4, w4
+        if args.config != 3:
+            extra.update(_extra_prefill(stream, steps2))
             torch.cuda.empty_cache()
-        try:
-            log("mixed step: 128 decode + 4 prefill requests on one pool")
-            from position_agnostic_kv_lazy_amd.prepare import prepare
-            m5 = make_config(5)
-            k5, v5 = upload_pool(m5.prefill.k_pool, m5.prefill.v_pool)
-            dd = prepare(m5.decode, k5, v5)
-            dp = prepare(m5.prefill, k5, v5)
-            s2 = torch.cuda.Stream()
-            ev = torch.cuda.Event()
-
-            def pair():
-                ev.record(stream)
-                s2.wait_event(ev)
-                dp.run(s2)
-                dd.run(stream)
-                e2 = torch.cuda.Event()
-                e2.record(s2)
-                stream.wait_event(e2)
-
-            wall, pm, pmed, _ = time_launches(pair, steps2, 3, stream)
-            _, dm, _, _ = time_launches(lambda: dd.run(stream), steps2, 3, stream)
-            _, fm, _, _ = time_launches(lambda: dp.run(stream), steps2, 3, stream)
-            nb = m5.decode.logical_kv_bytes()
-            fl = m5.prefill.prefill_flops()
-            extra["mixed_step"] = {
-                "pair_event_ms_mean": round(pm, 5),
-                "decode_event_ms_mean": round(dm, 5),
-                "prefill_event_ms_mean": round(fm, 5),
-                "decode_gbs_logical": round(nb / (dm * 1e-3) / 1e9, 1),
-                "prefill_tflops": round(fl / (fm * 1e-3) / 1e12, 1),
-                "decode_logical_kv_bytes": nb, "prefill_flops": fl,
-            }
-        except Exception as e:
-            extra["mixed_step"] = {"error": repr(e)}
+        if args.config != 4:
+            extra.update(_extra_long_decode(stream, steps2))
+            torch.cuda.empty_cache()
+        extra.update(_extra_mixed(stream, steps2))
     result["extra"] = extra
 
     if not args.no_cpu:
