@@ -290,17 +290,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     }
 
     // ---- S'^T = K' Q^T - m for this wave's 32 rows x 64 keys
+    // The two 32-key accumulators alternate, so consecutive MFMAs are independent.
     f32x16 sacc[2];
 #pragma unroll
-    for (int tk = 0; tk < 2; ++tk) {
-      const int key = 32 * tk + col;
+    for (int tk = 0; tk < 2; ++tk)
       sacc[tk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_a, negm_b, f32x16{}, 0, 0, 0);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[buf][k_lds_off(key, 2 * s + h2)]);
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int tk = 0; tk < 2; ++tk) {
+        const uint4 a =
+            *reinterpret_cast<const uint4*>(&k_lds[buf][k_lds_off(32 * tk + col, 2 * s + h2)]);
         sacc[tk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qb[s], sacc[tk], 0, 0, 0);
       }
-    }
     // sacc[tk][rr] = score(key 32tk + 8(rr/4) + 4h2 + rr%4, this lane's row) - mref
     if (!tile_simple) {
       // Visible slots of block bb are [0, lim[bb]).  Routing the limits through
@@ -367,15 +369,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     lrun += psum;
 
     // ---- O^T += V^T P^T
+    // The four output tiles alternate, so consecutive MFMAs are independent.
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int dim = 32 * t + col;
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&v_lds[buf][v_lds_off(dim, 2 * u + h2)]);
+      for (int t = 0; t < 4; ++t) {
+        const uint4 a =
+            *reinterpret_cast<const uint4*>(&v_lds[buf][v_lds_off(32 * t + col, 2 * u + h2)]);
         oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[u], oacc[t], 0, 0, 0);
       }
-    }
     if (more) store_tile(st, buf ^ 1);
     __syncthreads();
   }
