@@ -92,6 +92,27 @@ typedef enum la_status {
 
 typedef enum la_dtype { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
 
+/*
+ * What k_pool holds.
+ *  LA_POOL_POSITION_FREE (default): keys without positional encoding; the
+ *    kernels rotate every key at its logical position (deferred encoding,
+ *    §3.1).  Block words carry pos0 = logical position of slot 0.
+ *  LA_POOL_DOC_LOCAL: each key stored pre-rotated by its index t within its
+ *    segment (R_t k, "indexing from position 0", §3.2 "Prefilling" and
+ *    Example 3.1).  Words of cached (non-causal) blocks carry pos0 = the
+ *    segment's logical start s for every block of the segment, and the score
+ *    (R_m q)^T (R_{s+t} k) is computed as (R_{m-s} q)^T (R_t k) in decode --
+ *    one rotation of q per segment, none of the keys (§3.2 "Decoding",
+ *    Eq. 6) -- and as (R_m q)^T (R_s (R_t k)) in prefill -- one relative
+ *    rotation per key, with one cos/sin row per segment (§3.2 "Prefilling").
+ *    The new tokens of a prefill request form one causal segment starting at
+ *    q_pos0, stored as R_t k with t counted from q_pos0; its words keep slot
+ *    0's logical position (the causal mask needs it) and are rotated by
+ *    q_pos0.  Decode tables must not flag blocks causal in this mode.  A pool
+ *    pre-rotated at absolute positions is the special case s = 0.
+ */
+typedef enum la_pool_mode { LA_POOL_POSITION_FREE = 0, LA_POOL_DOC_LOCAL = 1 } la_pool_mode;
+
 /* Packing limits of the 64-bit block word. */
 #define LA_MAX_POSITION ((int64_t)1 << 24) /* positions must be < 2^24 */
 #define LA_MAX_BLOCK_ID ((int64_t)1 << 32)
@@ -107,7 +128,8 @@ typedef struct la_params {
   int32_t max_pos;       /* rows of cos_sin; every position must be < max_pos */
   int32_t split_blocks;  /* decode: blocks per split group, 0 = automatic */
   int32_t target_workgroups; /* decode split heuristic, 0 = 1024 (256 CUs x 4) */
-  int32_t reserved[5];   /* must be zero */
+  int32_t pool_mode;     /* la_pool_mode of k_pool (above) */
+  int32_t reserved[4];   /* must be zero */
 } la_params;
 
 /* Human-readable name of a status code (static string). */
@@ -144,7 +166,9 @@ LA_API la_status lazy_attn_rope_table(double base, int32_t head_dim, int32_t row
  *   max_blocks_per_req  host out (nullable): largest per-request block count
  * Checks block ids < num_blocks, positions < min(max_pos, 2^24), block counts,
  * and that every request has at least one token.  Returns LA_ERR_INVALID_ARG
- * (nothing written beyond what was checked) on violation.
+ * (nothing written beyond what was checked) on violation.  With
+ * LA_POOL_DOC_LOCAL the position field of every word of a cached segment is
+ * the segment start (new-token segments keep per-block positions).
  */
 LA_API la_status lazy_attn_pack_segments(const la_params* p, int32_t batch, const int64_t* req_seg_start,
                                   const int64_t* seg_start, const int64_t* seg_len,
@@ -161,7 +185,9 @@ LA_API la_status lazy_attn_pack_segments(const la_params* p, int32_t batch, cons
  *   cu_q    prefill: [batch+1] query row offsets; NULL for decode
  * Decode requires every key position < max_pos and q_pos < max_pos; prefill
  * requires q_pos + (cu_q[r+1]-cu_q[r]) - 1 < max_pos and that each new-token
- * row sees at least one key.
+ * row sees at least one key.  With LA_POOL_DOC_LOCAL, decode tables may not
+ * hold causal words and a prefill causal word must start a block of the
+ * new-token segment (pos0 - q_pos a multiple of block_size, >= 0).
  */
 LA_API la_status lazy_attn_validate_table(const la_params* p, int32_t batch, const uint64_t* blk_words,
                                    const int32_t* req_blk_start, const int32_t* q_pos,
@@ -174,6 +200,26 @@ LA_API la_status lazy_attn_validate_table(const la_params* p, int32_t batch, con
  */
 LA_API la_status lazy_attn_decode_workspace_size(const la_params* p, int32_t batch,
                                           int32_t max_blocks_per_req, size_t* bytes);
+
+/*
+ * Write n_tokens keys and values into pool slots (the cache write that
+ * precedes attention; keys are stored once and never re-encoded).
+ *   k, v       device [n_tokens][num_kv_heads][head_dim], pool dtype
+ *   slots      device int64 [n_tokens]: block_id * block_size + slot
+ *   rope_pos   device int32 [n_tokens] or NULL.  NULL stores keys as given
+ *              (position-free pool); otherwise key t is stored rotated,
+ *              R_{rope_pos[t]} k, computed in fp32 and rounded once -- e.g.
+ *              its index within its document for a LA_POOL_DOC_LOCAL pool
+ *   cos_sin    device [max_pos][2][head_dim/2] float32; rope_pos < max_pos
+ *              (may be NULL when rope_pos is NULL)
+ *   k_pool, v_pool  device, layouts above; V is written dim-major
+ * Slots must be distinct and < num_blocks * block_size (not checked on the
+ * device).  Asynchronous on stream.
+ */
+LA_API la_status lazy_attn_store_kv(const la_params* p, const void* k, const void* v,
+                                    int64_t n_tokens, const int64_t* slots,
+                                    const int32_t* rope_pos, const float* cos_sin, void* k_pool,
+                                    void* v_pool, void* stream);
 
 /*
  * Decode: one new query token per request attends exactly the request's

@@ -21,6 +21,7 @@ from .lazy_oracle import (  # noqa: F401
     attention_decode,
     attention_prefill,
     attention_decode_relative,
+    store_kv,
     run_decode,
     run_prefill,
 )

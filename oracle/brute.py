@@ -10,10 +10,11 @@ from __future__ import annotations
 
 import math
 
-__all__ = ["brute_attention"]
+__all__ = ["brute_attention", "brute_rotate"]
 
 
-def _rot(vec, pos, base):
+def brute_rotate(vec, pos, base):
+    """Rotate one vector (list) to position pos: pair (i, i + D/2) by pos * base^(-2i/D)."""
     D = len(vec)
     h = D // 2
     out = [0.0] * D
@@ -33,12 +34,12 @@ def brute_attention(queries, keys, scale, base):
     """
     res = []
     for qv, qp in queries:
-        qr = _rot(qv, qp, base)
+        qr = brute_rotate(qv, qp, base)
         scores, vals = [], []
         for kv, vv, kp, causal in keys:
             if causal and kp > qp:
                 continue
-            kr = _rot(kv, kp, base)
+            kr = brute_rotate(kv, kp, base)
             dot = 0.0
             for a, b in zip(qr, kr):
                 dot += a * b

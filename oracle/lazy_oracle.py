@@ -20,7 +20,11 @@ Readings of the pages (listed with reasons in the design notes):
   * scale 1/sqrt(D) multiplies the rotated q.k (Eq. 4);
   * GQA: query head h reads kv head floor(h / G) (§3.5 "GQA/MQA");
   * decode attends exactly the listed segments; prefill sees every cached
-    key and, among the new tokens, keys at positions <= the query's.
+    key and, among the new tokens, keys at positions <= the query's;
+  * a document-local pool (§3.2 "Prefilling": each document's cache indexed
+    from position 0; Example 3.1) holds R_t k for token t of a segment, so
+    its encoding at logical position s + t is R_s applied to what is stored
+    (R_s R_t = R_{s+t}); the oracle re-encodes stored keys that way.
 
 Inputs are the exact values handed to the GPU: bf16 pools/queries arrive as
 uint16 bit patterns and are widened exactly to float64 here.
@@ -36,6 +40,7 @@ __all__ = [
     "attention_decode",
     "attention_prefill",
     "attention_decode_relative",
+    "store_kv",
     "run_decode",
     "run_prefill",
 ]
@@ -105,6 +110,50 @@ def gather_request(k_pool, v_pool, segments, block_size: int, kv_head: int):
     return np.concatenate(ks), np.concatenate(vs), np.concatenate(ps), np.concatenate(ns)
 
 
+def _segment_starts(segments) -> np.ndarray:
+    """Logical start s of the segment of every gathered key, in gather order."""
+    parts = [np.full(int(seg.n_tokens), int(seg.start), np.int64) for seg in segments
+             if int(seg.n_tokens) > 0]
+    return np.concatenate(parts) if parts else np.zeros(0, np.int64)
+
+
+def _encode_keys(K, pos, segments, theta, doc_local):
+    """Keys encoded at their logical positions.
+
+    Position-free pool: R_p k.  Document-local pool (stored R_t k): R_s of the
+    stored key, s = the segment's start, which is R_{s+t} k.
+    """
+    if doc_local:
+        return rope_rotate(K, _segment_starts(segments), theta)
+    return rope_rotate(K, pos, theta)
+
+
+def store_kv(k, v, slots, rope_pos, k_pool, v_pool, *, block_size, theta):
+    """The cache write: new tokens' keys and values into pool slots.
+
+    Token n goes to block slots[n] // BS, slot slots[n] % BS; its key is
+    stored as given (rope_pos None: the position-free pool of §3.1 "Deferred
+    encoding") or rotated to rope_pos[n] (R_p k; p = the index inside its
+    document for a document-local pool, §3.2 "Prefilling"), its value as
+    given.  Returns float64 copies of the logical [nb, Hkv, BS, D] pools;
+    slots not listed keep their old contents.
+
+    Pins: rope_pos None is an exact copy; a rotated key equals the complex
+    product x * exp(j p theta) and keeps its norm; Example 3.1 through
+    attention (tests/test_oracle.py).
+    """
+    kp = _as_f64(k_pool).copy()
+    vp = _as_f64(v_pool).copy()
+    kf, vf = _as_f64(k), _as_f64(v)
+    slots = np.asarray(slots, np.int64)
+    blk, sl = slots // block_size, slots % block_size
+    if rope_pos is not None:
+        kf = rope_rotate(kf, np.asarray(rope_pos, np.int64)[:, None], theta)
+    kp[blk, :, sl, :] = kf
+    vp[blk, :, sl, :] = vf
+    return kp, vp
+
+
 def _softmax_attend(scores: np.ndarray, V: np.ndarray):
     """Textbook softmax over the last axis (Eq. 4), returning (out, lse)."""
     if scores.shape[-1] == 0:
@@ -120,13 +169,14 @@ def _softmax_attend(scores: np.ndarray, V: np.ndarray):
 
 
 def attention_decode(q, q_pos, segments, k_pool, v_pool, *, block_size, num_kv_heads,
-                     theta, scale, rotate=True):
+                     theta, scale, rotate=True, doc_local=False):
     """One decode query (all heads) of one request, eager RoPE.
 
     q: [Hq, D]; q_pos: the query's logical position m.  Keys are gathered,
     re-encoded at their positions (the materialised cache the method avoids)
     and attended with textbook softmax.  Returns out [Hq, D], lse [Hq].
-    rotate=False drops RoPE entirely (used by the identity-table pin).
+    rotate=False drops RoPE entirely (used by the identity-table pin);
+    doc_local=True reads a document-local pool (stored keys R_t k).
     """
     qf = _as_f64(q)
     Hq, D = qf.shape
@@ -137,7 +187,7 @@ def attention_decode(q, q_pos, segments, k_pool, v_pool, *, block_size, num_kv_h
         K, V, pos, _ = gather_request(k_pool, v_pool, segments, block_size, g)
         qs = qf[g * G:(g + 1) * G]
         if rotate:
-            Kt = rope_rotate(K, pos, theta)
+            Kt = _encode_keys(K, pos, segments, theta, doc_local)
             qt = rope_rotate(qs, np.full(G, q_pos), theta)
         else:
             Kt, qt = K, qs
@@ -172,13 +222,14 @@ def attention_decode_relative(q, q_pos, segments, k_pool, v_pool, *, block_size,
 
 
 def attention_prefill(q, q_pos0, segments, k_pool, v_pool, *, block_size, num_kv_heads,
-                      theta, scale, rotate=True, rows=None):
+                      theta, scale, rotate=True, rows=None, doc_local=False):
     """New-token attention of one request, eager RoPE.
 
     q: [T, Hq, D]; new token j sits at position q_pos0 + j.  Keys of cached
     segments are all visible; keys of the new-token segment are visible iff
     their position is <= the query's.  rows optionally restricts the query
     rows computed (sampled parity).  Returns out [T', Hq, D], lse [T', Hq].
+    doc_local=True reads a document-local pool (stored keys R_t k).
     """
     qf = _as_f64(q)
     T, Hq, D = qf.shape
@@ -189,7 +240,7 @@ def attention_prefill(q, q_pos0, segments, k_pool, v_pool, *, block_size, num_kv
     lse = np.empty((len(rows), Hq))
     for g in range(num_kv_heads):
         K, V, pos, new = gather_request(k_pool, v_pool, segments, block_size, g)
-        Kt = rope_rotate(K, pos, theta) if rotate else K
+        Kt = _encode_keys(K, pos, segments, theta, doc_local) if rotate else K
         visible = (~new)[None, :] | (pos[None, :] <= qpos[:, None])  # [T', n]
         for hh in range(G):
             h = g * G + hh
@@ -207,30 +258,38 @@ def _theta_of(w):
     return rope_theta(w.head_dim, w.rope_base)
 
 
-def run_decode(w, requests=None, rotate=True):
-    """Oracle outputs for decode workload w: {r: (out [Hq, D], lse [Hq])}."""
+def run_decode(w, requests=None, rotate=True, pools=None, doc_local=False):
+    """Oracle outputs for decode workload w: {r: (out [Hq, D], lse [Hq])}.
+
+    pools, if given, replaces (w.k_pool, w.v_pool), e.g. by a document-local
+    pool written with store_kv (then doc_local=True).
+    """
     th = _theta_of(w)
+    kp, vp = (w.k_pool, w.v_pool) if pools is None else pools
     reqs = range(w.batch) if requests is None else requests
     res = {}
     for r in reqs:
-        res[r] = attention_decode(w.q[r], int(w.q_pos[r]), w.requests[r], w.k_pool, w.v_pool,
+        res[r] = attention_decode(w.q[r], int(w.q_pos[r]), w.requests[r], kp, vp,
                                   block_size=w.block_size, num_kv_heads=w.num_kv_heads,
-                                  theta=th, scale=w.scale, rotate=rotate)
+                                  theta=th, scale=w.scale, rotate=rotate, doc_local=doc_local)
     return res
 
 
-def run_prefill(w, requests=None, rows=None, rotate=True):
+def run_prefill(w, requests=None, rows=None, rotate=True, pools=None, doc_local=False):
     """Oracle outputs for prefill workload w: {r: (out [T', Hq, D], lse [T', Hq])}.
 
-    rows, if given, maps request -> array of new-token indices to compute.
+    rows, if given, maps request -> array of new-token indices to compute;
+    pools / doc_local as for run_decode.
     """
     th = _theta_of(w)
+    kp, vp = (w.k_pool, w.v_pool) if pools is None else pools
     reqs = range(w.batch) if requests is None else requests
     res = {}
     for r in reqs:
         a, b = int(w.cu_q[r]), int(w.cu_q[r + 1])
         rr = None if rows is None else rows.get(r)
-        res[r] = attention_prefill(w.q[a:b], int(w.q_pos[r]), w.requests[r], w.k_pool, w.v_pool,
+        res[r] = attention_prefill(w.q[a:b], int(w.q_pos[r]), w.requests[r], kp, vp,
                                    block_size=w.block_size, num_kv_heads=w.num_kv_heads,
-                                   theta=th, scale=w.scale, rotate=rotate, rows=rr)
+                                   theta=th, scale=w.scale, rotate=rotate, rows=rr,
+                                   doc_local=doc_local)
     return res

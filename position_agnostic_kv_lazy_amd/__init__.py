@@ -9,6 +9,8 @@ functions carry the C names.
 from .binding import (  # noqa: F401
     LA_BF16,
     LA_FP32,
+    LA_POOL_POSITION_FREE,
+    LA_POOL_DOC_LOCAL,
     LazyAttnError,
     la_params,
     make_params,
@@ -18,6 +20,7 @@ from .binding import (  # noqa: F401
     lazy_attn_pack_segments,
     lazy_attn_validate_table,
     lazy_attn_decode_workspace_size,
+    lazy_attn_store_kv,
     lazy_attn_decode,
     lazy_attn_prefill,
 )

@@ -19,13 +19,21 @@ LIB_PATH = os.environ.get("LAZYATTN_LIB", os.path.join(_PKG, "liblazyattn.so"))
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} not found: build it with `python -m position_agnostic_kv_lazy_amd.build` "
+        f"{LIB_PATH} not found: build it with `python position_agnostic_kv_lazy_amd/build.py` "
         "(or __graft_entry__.build())")
+
+# PyTorch ships its own libamdhip64 under the same soname as ROCm's.  Loading
+# torch first makes the loader bind this library's libamdhip64.so.7 to that
+# copy, so both share one HIP runtime (one device context, one set of streams
+# and allocations).  Loaded the other way round, the process would hold two
+# independent HIP runtimes and this library could not see torch's device.
+import torch  # noqa: E402,F401
 
 _lib = ctypes.CDLL(LIB_PATH)
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE_TOO_SMALL, LA_ERR_HIP = range(5)
 LA_BF16, LA_FP32 = 0, 1
+LA_POOL_POSITION_FREE, LA_POOL_DOC_LOCAL = 0, 1
 
 EXPORTED = (
     "lazy_attn_status_string",
@@ -34,6 +42,7 @@ EXPORTED = (
     "lazy_attn_pack_segments",
     "lazy_attn_validate_table",
     "lazy_attn_decode_workspace_size",
+    "lazy_attn_store_kv",
     "lazy_attn_decode",
     "lazy_attn_prefill",
 )
@@ -51,7 +60,8 @@ class la_params(ctypes.Structure):
         ("max_pos", ctypes.c_int32),
         ("split_blocks", ctypes.c_int32),
         ("target_workgroups", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 5),
+        ("pool_mode", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 4),
     ]
 
 
@@ -85,6 +95,8 @@ _lib.lazy_attn_validate_table.argtypes = [_prm, ctypes.c_int32, _P, _P, _P, _P]
 _lib.lazy_attn_decode_workspace_size.restype = ctypes.c_int
 _lib.lazy_attn_decode_workspace_size.argtypes = [_prm, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.POINTER(ctypes.c_size_t)]
+_lib.lazy_attn_store_kv.restype = ctypes.c_int
+_lib.lazy_attn_store_kv.argtypes = [_prm, _P, _P, ctypes.c_int64, _P, _P, _P, _P, _P, _P]
 _lib.lazy_attn_decode.restype = ctypes.c_int
 _lib.lazy_attn_decode.argtypes = [_prm, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                   _P, _P, _P, ctypes.c_size_t, _P]
@@ -99,7 +111,7 @@ def _check(status: int, func: str):
 
 
 def make_params(*, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, scale,
-                max_pos, split_blocks=0, target_workgroups=0) -> la_params:
+                max_pos, split_blocks=0, target_workgroups=0, pool_mode=0) -> la_params:
     p = la_params()
     p.num_q_heads = num_q_heads
     p.num_kv_heads = num_kv_heads
@@ -111,6 +123,8 @@ def make_params(*, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, 
     p.max_pos = max_pos
     p.split_blocks = split_blocks
     p.target_workgroups = target_workgroups
+    p.pool_mode = {"position_free": LA_POOL_POSITION_FREE,
+                   "doc_local": LA_POOL_DOC_LOCAL}.get(pool_mode, pool_mode)
     return p
 
 
@@ -203,6 +217,13 @@ def lazy_attn_decode_workspace_size(params: la_params, batch: int, max_blocks_pe
     _check(_lib.lazy_attn_decode_workspace_size(ctypes.byref(params), batch, max_blocks_per_req,
                                                 ctypes.byref(n)), "lazy_attn_decode_workspace_size")
     return int(n.value)
+
+
+def lazy_attn_store_kv(params: la_params, k, v, n_tokens: int, slots, rope_pos, cos_sin, k_pool,
+                       v_pool, stream=None):
+    _check(_lib.lazy_attn_store_kv(ctypes.byref(params), _ptr(k), _ptr(v), int(n_tokens),
+                                   _ptr(slots), _ptr(rope_pos), _ptr(cos_sin), _ptr(k_pool),
+                                   _ptr(v_pool), _stream(stream)), "lazy_attn_store_kv")
 
 
 def lazy_attn_decode(params: la_params, q, k_pool, v_pool, blk_words, req_blk_start, q_pos,

@@ -1,6 +1,8 @@
 """Build liblazyattn.so in-tree with hipcc for gfx950.
 
-    python -m position_agnostic_kv_lazy_amd.build
+    python position_agnostic_kv_lazy_amd/build.py
+
+(run as a script: importing the package loads the library being rebuilt).
 
 Every HIP source is compiled with -Xclang -target-feature -Xclang
 -packed-fp32-ops, so the device compiler never emits packed fp32 arithmetic;
@@ -21,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblazyattn.so")
 
-SOURCES = ["lazy_attn_host.cpp", "attn_f32.hip", "decode_bf16.hip", "prefill_bf16.hip"]
+SOURCES = ["lazy_attn_host.cpp", "attn_f32.hip", "decode_bf16.hip", "prefill_bf16.hip", "store_kv.hip"]
 ARCH = os.environ.get("LAZYATTN_ARCH", "gfx950")
 
 

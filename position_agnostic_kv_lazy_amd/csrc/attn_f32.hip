@@ -6,13 +6,18 @@
 // "LazyAttention" §3.1), the query to its position, and an online softmax in
 // fp32 accumulates the output.  Used for the 1e-5 parity mode; the bf16
 // kernels are the fast path.
+//
+// Document-local pools (keys stored as R_t k with t the index inside the
+// segment): decode rotates q by m - s per block (s = the segment start the word
+// carries) and uses the keys as stored; prefill rotates each key by s once
+// (for the causal blocks s is the request's first new position).
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace lazyattn {
 namespace {
 
-template <int D>
+template <int D, bool DOC_LOCAL>
 __global__ __launch_bounds__(64) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k_pool,
     const float* __restrict__ v_pool, const uint64_t* __restrict__ words,
@@ -23,8 +28,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
   const int h = blockIdx.x;
   const int r = blockIdx.z;
   const int lane = threadIdx.x;
+  const bool prefill = cu_q != nullptr;
   int row, qp;
-  if (cu_q != nullptr) {  // prefill: blockIdx.y is the new-token index
+  if (prefill) {  // blockIdx.y is the new-token index
     const int j = blockIdx.y;
     const int a = cu_q[r];
     if (j >= cu_q[r + 1] - a) return;
@@ -38,15 +44,18 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
   const bool active = lane < HALF;
   const int i = active ? lane : 0;
 
-  // Query rotated to its own position m.
+  // Query rotated to its own position m (doc-local pools: per block, below).
   const float* qrow = q + (static_cast<size_t>(row) * Hq + h) * D;
-  float q1 = 0.f, q2 = 0.f;
+  float q1 = 0.f, q2 = 0.f, x1 = 0.f, x2 = 0.f;
   if (active) {
-    const float x1 = qrow[i], x2 = qrow[i + HALF];
-    const float c = cs[static_cast<size_t>(qp) * D + i];
-    const float s = cs[static_cast<size_t>(qp) * D + HALF + i];
-    q1 = x1 * c - x2 * s;
-    q2 = x1 * s + x2 * c;
+    x1 = qrow[i];
+    x2 = qrow[i + HALF];
+    if (!DOC_LOCAL || prefill) {
+      const float c = cs[static_cast<size_t>(qp) * D + i];
+      const float s = cs[static_cast<size_t>(qp) * D + HALF + i];
+      q1 = x1 * c - x2 * s;
+      q2 = x1 * s + x2 * c;
+    }
   }
 
   float m = -INFINITY, l = 0.f, acc1 = 0.f, acc2 = 0.f;
@@ -56,15 +65,29 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
     const size_t tile = static_cast<size_t>(w.block_id) * Hkv + g;
     const float* kb = k_pool + tile * BS * D;
     const float* vb = v_pool + tile * D * BS;
+    if (DOC_LOCAL && !prefill && active) {  // q_s = R_{m - s} q; R_{-x} negates the sine
+      const int off = qp - w.pos0;
+      const size_t r0 = static_cast<size_t>(off < 0 ? -off : off) * D;
+      const float c = cs[r0 + i];
+      const float s = (off < 0 ? -1.f : 1.f) * cs[r0 + HALF + i];
+      q1 = x1 * c - x2 * s;
+      q2 = x1 * s + x2 * c;
+    }
     for (int t = 0; t < w.n_valid; ++t) {
       const int p = w.pos0 + t;
-      if (cu_q != nullptr && w.causal && p > qp) break;  // later slots are later positions
+      if (prefill && w.causal && p > qp) break;  // later slots are later positions
       float part = 0.f, v1 = 0.f, v2 = 0.f;
       if (active) {
         const float k1 = kb[t * D + i], k2 = kb[t * D + i + HALF];
-        const float c = cs[static_cast<size_t>(p) * D + i];
-        const float s = cs[static_cast<size_t>(p) * D + HALF + i];
-        part = q1 * (k1 * c - k2 * s) + q2 * (k1 * s + k2 * c);
+        if (DOC_LOCAL && !prefill) {
+          part = q1 * k1 + q2 * k2;
+        } else {
+          // key rotation: its position, or (doc-local) its segment's start
+          const int pr = !DOC_LOCAL ? p : (w.causal ? q_pos[r] : w.pos0);
+          const float c = cs[static_cast<size_t>(pr) * D + i];
+          const float s = cs[static_cast<size_t>(pr) * D + HALF + i];
+          part = q1 * (k1 * c - k2 * s) + q2 * (k1 * s + k2 * c);
+        }
         v1 = vb[i * BS + t];
         v2 = vb[(i + HALF) * BS + t];
       }
@@ -92,16 +115,17 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 hipError_t launch_attn_f32(const AttnArgs& a, bool prefill, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, prefill ? a.max_q_per_req : 1, a.batch);
   const int32_t* cu = prefill ? a.cu_q : nullptr;
-#define LAZYATTN_F32(DIM)                                                                    \
-  hipLaunchKernelGGL(attn_f32_kernel<DIM>, grid, dim3(64), 0, stream,                        \
+#define LAZYATTN_F32(DIM, DOC)                                                               \
+  hipLaunchKernelGGL((attn_f32_kernel<DIM, DOC>), grid, dim3(64), 0, stream,                 \
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k_pool),    \
                      static_cast<const float*>(a.v_pool), a.words, a.req_blk_start, cu,      \
                      a.q_pos, a.cos_sin, a.num_q_heads, a.num_kv_heads, a.block_size,         \
                      a.scale, static_cast<float*>(a.out), a.lse)
+  const bool doc = a.pool_mode == 1;
   if (a.head_dim == 128) {
-    LAZYATTN_F32(128);
+    if (doc) LAZYATTN_F32(128, true); else LAZYATTN_F32(128, false);
   } else if (a.head_dim == 64) {
-    LAZYATTN_F32(64);
+    if (doc) LAZYATTN_F32(64, true); else LAZYATTN_F32(64, false);
   } else {
     return hipErrorInvalidValue;
   }

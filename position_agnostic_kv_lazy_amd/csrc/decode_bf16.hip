@@ -27,6 +27,14 @@
 // exactly the B-operand layout of the P.V product, so P never leaves the lane.
 // V tiles are stored dim-major in the pool so the A operand of P.V (4
 // consecutive keys of one dim) is one 8-byte load.
+//
+// Document-local pools (keys stored pre-rotated by their index within their
+// segment, block words carrying the segment start s): the score is
+// (R_{m-s} q)^T k_stored, so keys are used as loaded and q is rotated only when
+// s changes between consecutive blocks of a wave -- once per document run, the
+// decode design of the paper's §3.2 (Eq. 6).
+#include <climits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -47,7 +55,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ i16x4 as_i16x4(uint2 u) { return __builtin_bit_cast(i16x4, u); }
 
-template <int G>
+template <int G, bool DOC_LOCAL>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const uint64_t* __restrict__ words,
@@ -81,7 +89,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
   // Slot rotation of the key slot this lane owns: pairs j = 8*(4s+gq) + e.
   float cslot[2][8], sslot[2][8];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < 2 && !DOC_LOCAL; ++s) {
     const float* row = cs + static_cast<size_t>(n) * D + 8 * (4 * s + gq);
     const float4 c0 = *reinterpret_cast<const float4*>(row);
     const float4 c1 = *reinterpret_cast<const float4*>(row + 4);
@@ -107,6 +115,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
   }
 
   float mrun = -INFINITY, lrun = 0.f;
+  int q_delta = INT_MIN;  // doc-local pools: segment start qbv was rotated for
+  bf16x8 qbv[4];          // Q_b^T as the B operand: column n = head n (zero beyond G)
   f32x4 oacc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -124,40 +134,59 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) vr[j] = *reinterpret_cast<const uint2*>(vb + 16 * j * BS);
 
-    // q_b = R_{m - pos0} q for this block; R_{-x} has the sine negated.
-    int off = m - w.pos0;
-    float sgn = 1.f;
-    if (off < 0) {
-      off = -off;
-      sgn = -1.f;
-    }
-    {
-      const float* row = cs + static_cast<size_t>(off) * D + pg * G;
-      uint16_t* dst = &qb_lds[wave][hh][0];
+    // q_b = R_{m - pos0} q for this block (doc-local pools: R_{m - s}, only when
+    // the segment changes); R_{-x} has the sine negated.
+    const bool rotate_q = !DOC_LOCAL || w.pos0 != q_delta;
+    if (rotate_q) {
+      q_delta = w.pos0;
+      int off = m - w.pos0;
+      float sgn = 1.f;
+      if (off < 0) {
+        off = -off;
+        sgn = -1.f;
+      }
+      {
+        const float* row = cs + static_cast<size_t>(off) * D + pg * G;
+        uint16_t* dst = &qb_lds[wave][hh][0];
 #pragma unroll
-      for (int u = 0; u < G; u += 2) {
-        float y1[2], y2[2];
+        for (int u = 0; u < G; u += 2) {
+          float y1[2], y2[2];
 #pragma unroll
-        for (int t = 0; t < 2 && u + t < G; ++t) {
-          const float c = row[u + t];
-          const float sn = sgn * row[HALF + u + t];
-          y1[t] = qx1[u + t] * c - qx2[u + t] * sn;
-          y2[t] = qx1[u + t] * sn + qx2[u + t] * c;
-        }
-        if (G == 1) {
-          dst[pg * G + u] = f32_to_bf16(y1[0]);
-          dst[HALF + pg * G + u] = f32_to_bf16(y2[0]);
-        } else {
-          *reinterpret_cast<uint32_t*>(dst + pg * G + u) = pack_bf16x2(y1[0], y1[1]);
-          *reinterpret_cast<uint32_t*>(dst + HALF + pg * G + u) = pack_bf16x2(y2[0], y2[1]);
+          for (int t = 0; t < 2 && u + t < G; ++t) {
+            const float c = row[u + t];
+            const float sn = sgn * row[HALF + u + t];
+            y1[t] = qx1[u + t] * c - qx2[u + t] * sn;
+            y2[t] = qx1[u + t] * sn + qx2[u + t] * c;
+          }
+          if (G == 1) {
+            dst[pg * G + u] = f32_to_bf16(y1[0]);
+            dst[HALF + pg * G + u] = f32_to_bf16(y2[0]);
+          } else {
+            *reinterpret_cast<uint32_t*>(dst + pg * G + u) = pack_bf16x2(y1[0], y1[1]);
+            *reinterpret_cast<uint32_t*>(dst + HALF + pg * G + u) = pack_bf16x2(y2[0], y2[1]);
+          }
         }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint4 v = uint4{0u, 0u, 0u, 0u};
+        if (n < G) v = *reinterpret_cast<const uint4*>(&qb_lds[wave][n < G ? n : 0][8 * (4 * s + gq)]);
+        qbv[s] = as_bf16x8(v);
+      }
+      __builtin_amdgcn_wave_barrier();
     }
 
-    // K' = R_slot k (fp32), rounded to bf16 for the MFMA.
+    // K' = R_slot k (fp32), rounded to bf16 for the MFMA (doc-local: as stored).
     bf16x8 ka[4];
+    if (DOC_LOCAL) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < 4; ++s) ka[s] = as_bf16x8(kr[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < 2 && !DOC_LOCAL; ++s) {
       const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&kr[s]);
       const uint32_t* a2 = reinterpret_cast<const uint32_t*>(&kr[s + 2]);
       uint4 o1, o2;
@@ -180,19 +209,6 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
       ka[s] = as_bf16x8(o1);
       ka[s + 2] = as_bf16x8(o2);
     }
-
-    // Q_b^T as the B operand: column n = head n (zero beyond G).
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    bf16x8 qbv[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint4 v = uint4{0u, 0u, 0u, 0u};
-      if (n < G) v = *reinterpret_cast<const uint4*>(&qb_lds[wave][n < G ? n : 0][8 * (4 * s + gq)]);
-      qbv[s] = as_bf16x8(v);
-    }
-    __builtin_amdgcn_wave_barrier();
 
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -312,7 +328,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   if (lse != nullptr && lane == 0) lse[rh] = L > 0.f ? (M + __log2f(L)) * LN2 : -INFINITY;
 }
 
-template <int G>
+template <int G, bool DOC_LOCAL>
 hipError_t launch_g(const AttnArgs& a, const DecodeSplit& s, void* ws, hipStream_t stream) {
   const int npairs = a.batch * a.num_kv_heads;
   float* part_o = nullptr;
@@ -322,7 +338,8 @@ hipError_t launch_g(const AttnArgs& a, const DecodeSplit& s, void* ws, hipStream
     part_ml = part_o + static_cast<size_t>(a.batch) * a.num_q_heads * s.groups * D;
   }
   const float qscale = a.scale * LOG2E;
-  hipLaunchKernelGGL(decode_bf16_kernel<G>, dim3(npairs * s.groups), dim3(256), 0, stream,
+  hipLaunchKernelGGL((decode_bf16_kernel<G, DOC_LOCAL>), dim3(npairs * s.groups), dim3(256), 0,
+                     stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
                      static_cast<const uint16_t*>(a.v_pool), a.words, a.req_blk_start, a.q_pos,
                      a.cos_sin, a.num_kv_heads, npairs, s.groups, s.group_blocks, qscale, part_o,
@@ -364,12 +381,13 @@ size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, const De
 
 hipError_t launch_decode_bf16(const AttnArgs& a, const DecodeSplit& s, void* workspace,
                               hipStream_t stream) {
+  const bool doc = a.pool_mode == 1;
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_g<1>(a, s, workspace, stream);
-    case 2: return launch_g<2>(a, s, workspace, stream);
-    case 4: return launch_g<4>(a, s, workspace, stream);
-    case 8: return launch_g<8>(a, s, workspace, stream);
-    case 16: return launch_g<16>(a, s, workspace, stream);
+    case 1: return doc ? launch_g<1, true>(a, s, workspace, stream) : launch_g<1, false>(a, s, workspace, stream);
+    case 2: return doc ? launch_g<2, true>(a, s, workspace, stream) : launch_g<2, false>(a, s, workspace, stream);
+    case 4: return doc ? launch_g<4, true>(a, s, workspace, stream) : launch_g<4, false>(a, s, workspace, stream);
+    case 8: return doc ? launch_g<8, true>(a, s, workspace, stream) : launch_g<8, false>(a, s, workspace, stream);
+    case 16: return doc ? launch_g<16, true>(a, s, workspace, stream) : launch_g<16, false>(a, s, workspace, stream);
     default: return hipErrorInvalidValue;
   }
 }

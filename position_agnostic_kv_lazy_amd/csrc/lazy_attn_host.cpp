@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <climits>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -59,8 +60,10 @@ la_status check_params(const la_params* p) {
   if (!std::isfinite(p->scale)) return fail(LA_ERR_INVALID_ARG, "scale is not finite");
   if (p->split_blocks < 0 || p->target_workgroups < 0)
     return fail(LA_ERR_INVALID_ARG, "split_blocks / target_workgroups must be >= 0");
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 4; ++i)
     if (p->reserved[i] != 0) return fail(LA_ERR_INVALID_ARG, "reserved fields must be zero");
+  if (p->pool_mode != LA_POOL_POSITION_FREE && p->pool_mode != LA_POOL_DOC_LOCAL)
+    return fail(LA_ERR_INVALID_ARG, "unknown pool_mode %d", p->pool_mode);
   if (p->dtype == LA_FP32) {
     if (p->head_dim != 64 && p->head_dim != 128)
       return fail(LA_ERR_UNSUPPORTED, "fp32 mode supports head_dim 64 or 128, got %d",
@@ -113,6 +116,7 @@ lazyattn::AttnArgs make_args(const la_params* p, const void* q, const void* k_po
   a.max_q_per_req = max_q;
   a.max_blocks_per_req = max_blocks;
   a.scale = p->scale;
+  a.pool_mode = p->pool_mode;
   return a;
 }
 
@@ -224,7 +228,11 @@ LA_API la_status lazy_attn_pack_segments(const la_params* p, int32_t batch,
           if (w >= capacity)
             return fail(LA_ERR_INVALID_ARG, "blk_words capacity %lld too small", (long long)capacity);
           const int nv = static_cast<int>(k + 1 < nb ? BS : n - k * BS);
-          blk_words[w++] = pack_word(id, start + k * BS, nv, seg_is_new[s] != 0);
+          // doc-local pools: cached segments carry their start s; new-token
+          // (causal) segments keep per-block positions for the causal mask
+          const bool doc = p->pool_mode == LA_POOL_DOC_LOCAL && seg_is_new[s] == 0;
+          const int64_t pos = doc ? start : start + k * BS;
+          blk_words[w++] = pack_word(id, pos, nv, seg_is_new[s] != 0);
         }
         tokens += n;
       }
@@ -278,9 +286,20 @@ LA_API la_status lazy_attn_validate_table(const la_params* p, int32_t batch,
           return fail(LA_ERR_INVALID_ARG, "row %d: block id %lld >= num_blocks", b, (long long)id);
         if (nv > p->block_size)
           return fail(LA_ERR_INVALID_ARG, "row %d: n_valid %d > block_size", b, nv);
-        if (pos0 + nv - 1 >= p->max_pos)
+        // Doc-local cached words carry the segment start, which must itself be
+        // a valid position; all other words carry slot 0's position.
+        const bool doc = p->pool_mode == LA_POOL_DOC_LOCAL;
+        const int64_t last = doc && !causal ? pos0 : pos0 + nv - 1;
+        if (last >= p->max_pos)
           return fail(LA_ERR_INVALID_ARG, "row %d: position %lld >= max_pos %d", b,
-                      (long long)(pos0 + nv - 1), p->max_pos);
+                      (long long)last, p->max_pos);
+        if (doc && causal && !cu_q)
+          return fail(LA_ERR_INVALID_ARG,
+                      "row %d: doc-local decode tables must not flag blocks causal", b);
+        if (doc && causal && (pos0 < m0 || (pos0 - m0) % p->block_size != 0))
+          return fail(LA_ERR_INVALID_ARG,
+                      "row %d: doc-local causal block at %lld does not start a block of the "
+                      "new-token segment at %lld", b, (long long)pos0, (long long)m0);
         if (causal && cu_q) {
           if (pos0 < min_causal) min_causal = pos0;
         } else {
@@ -311,6 +330,32 @@ LA_API la_status lazy_attn_decode_workspace_size(const la_params* p, int32_t bat
       batch, p->num_kv_heads, max_blocks_per_req, p->split_blocks, p->target_workgroups);
   *bytes = lazyattn::decode_workspace_bytes(batch, p->num_q_heads, p->head_dim, s);
   return ok();
+}
+
+LA_API la_status lazy_attn_store_kv(const la_params* p, const void* k, const void* v,
+                                    int64_t n_tokens, const int64_t* slots,
+                                    const int32_t* rope_pos, const float* cos_sin, void* k_pool,
+                                    void* v_pool, void* stream) {
+  try {
+    la_status st = check_params(p);
+    if (st != LA_OK) return st;
+    if (n_tokens < 0 || n_tokens > INT32_MAX)
+      return fail(LA_ERR_INVALID_ARG, "n_tokens %lld outside [0, 2^31)", (long long)n_tokens);
+    if (p->num_kv_heads > 65535)
+      return fail(LA_ERR_UNSUPPORTED, "store_kv supports at most 65535 kv heads");
+    if (n_tokens == 0) return ok();
+    if (!k || !v || !slots || !k_pool || !v_pool)
+      return fail(LA_ERR_INVALID_ARG, "NULL device pointer passed to lazy_attn_store_kv");
+    if (rope_pos && !cos_sin)
+      return fail(LA_ERR_INVALID_ARG, "rope_pos given without cos_sin");
+    const hipError_t e = lazyattn::launch_store_kv(
+        k, v, n_tokens, slots, rope_pos, cos_sin, p->num_kv_heads, p->head_dim, p->block_size,
+        p->dtype == LA_BF16, k_pool, v_pool, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "lazy_attn_store_kv launch");
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_HIP, "unexpected exception in lazy_attn_store_kv");
+  }
 }
 
 LA_API la_status lazy_attn_decode(const la_params* p, const void* q, const void* k_pool,

@@ -25,6 +25,12 @@
 // LDS in the key order that makes each lane's 8-key A operand one 16-byte read.
 // Causal masking is applied only on blocks flagged causal (the new tokens);
 // trailing causal blocks no row of the workgroup can see are skipped.
+//
+// Document-local pools (keys stored as R_t k, t = index inside the segment):
+// every key of a block is rotated by the same offset s, the segment start its
+// word carries (for causal blocks, whose words keep slot 0's position for the
+// mask, s is the request's first new position), so one table row serves a
+// whole document -- the single relative rotation of §3.2 "Prefilling".
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -66,7 +72,7 @@ struct Staged {
   uint4 v[2];        // two 16-byte V^T chunks (unused slots zeroed)
 };
 
-template <int G>
+template <int G, bool DOC_LOCAL>
 __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const uint64_t* __restrict__ words,
@@ -176,9 +182,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     if (tb + kblk < rb1) {
       const BlockWord w = unpack_word(words[tb + kblk]);
       const uint16_t* kb = k_pool + (static_cast<size_t>(w.block_id) * Hkv + g) * (BS * D);
-      // unused slots keep K = 0 and read the table row of the block's last key
-      row = cs + static_cast<size_t>(w.pos0) * D +
-            static_cast<uint32_t>(min(kslot, w.n_valid - 1) * D + 8 * cp);
+      if (DOC_LOCAL) {
+        row = cs + static_cast<size_t>(w.causal ? p0 : w.pos0) * D + 8 * cp;
+      } else {
+        // unused slots keep K = 0 and read the table row of the block's last key
+        row = cs + static_cast<size_t>(w.pos0) * D +
+              static_cast<uint32_t>(min(kslot, w.n_valid - 1) * D + 8 * cp);
+      }
       if (kslot < w.n_valid) {
         const uint32_t off = static_cast<uint32_t>(kslot * D + 8 * cp);
         st.k1 = *reinterpret_cast<const uint4*>(kb + off);
@@ -402,12 +412,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
         lrun > 0.f ? (mref + __log2f(lrun)) * LN2 : -INFINITY;
 }
 
-template <int G>
+template <int G, bool DOC_LOCAL>
 hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
   constexpr int TQ = ROWS / G;
   const int npairs = a.batch * a.num_kv_heads;
   const int qtiles = (a.max_q_per_req + TQ - 1) / TQ;
-  hipLaunchKernelGGL(prefill_bf16_kernel<G>, dim3(npairs * qtiles), dim3(NTHREADS), 0, stream,
+  hipLaunchKernelGGL((prefill_bf16_kernel<G, DOC_LOCAL>), dim3(npairs * qtiles), dim3(NTHREADS), 0,
+                     stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
                      static_cast<const uint16_t*>(a.v_pool), a.words, a.req_blk_start, a.cu_q,
                      a.q_pos, a.cos_sin, a.num_kv_heads, npairs, a.scale * LOG2E,
@@ -418,12 +429,13 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
+  const bool doc = a.pool_mode == 1;
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_g<1>(a, stream);
-    case 2: return launch_g<2>(a, stream);
-    case 4: return launch_g<4>(a, stream);
-    case 8: return launch_g<8>(a, stream);
-    case 16: return launch_g<16>(a, stream);
+    case 1: return doc ? launch_g<1, true>(a, stream) : launch_g<1, false>(a, stream);
+    case 2: return doc ? launch_g<2, true>(a, stream) : launch_g<2, false>(a, stream);
+    case 4: return doc ? launch_g<4, true>(a, stream) : launch_g<4, false>(a, stream);
+    case 8: return doc ? launch_g<8, true>(a, stream) : launch_g<8, false>(a, stream);
+    case 16: return doc ? launch_g<16, true>(a, stream) : launch_g<16, false>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

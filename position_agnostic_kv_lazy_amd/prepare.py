@@ -85,15 +85,66 @@ class DeviceBatch:
         return o
 
 
+def params_for(w, num_blocks: int, max_pos: Optional[int] = None, split_blocks: int = 0,
+               target_workgroups: int = 0, pool_mode="position_free") -> B.la_params:
+    """la_params describing batch w over a pool of num_blocks blocks."""
+    rows = int(max_pos) if max_pos is not None else int(w.table_rows())
+    return B.make_params(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                         head_dim=w.head_dim, block_size=w.block_size, num_blocks=int(num_blocks),
+                         dtype=w.dtype, scale=w.scale, max_pos=rows, split_blocks=split_blocks,
+                         target_workgroups=target_workgroups, pool_mode=pool_mode)
+
+
+def store_pool(w, k_tok: np.ndarray, v_tok: np.ndarray, slots: np.ndarray,
+               rope_pos: Optional[np.ndarray], device="cuda", num_blocks: Optional[int] = None,
+               max_pos: Optional[int] = None, fill: float = 0.0, stream=None):
+    """Build a device pool pair by writing tokens with lazy_attn_store_kv.
+
+    k_tok / v_tok: host [n, Hkv, D] in the pool encoding; slots: flat slot ids;
+    rope_pos: per-token rotation position or None (keys stored as given).
+    Unlisted slots hold `fill`.  Returns (k_dev, v_dev) in the device layouts.
+    """
+    nb = int(num_blocks) if num_blocks is not None else int(w.num_blocks)
+    rows = int(max_pos) if max_pos is not None else int(w.table_rows())
+    slots = np.asarray(slots, np.int64)
+    # the kernel trusts slots and positions: check them here, before the launch
+    if slots.size and (slots.min() < 0 or slots.max() >= nb * w.block_size):
+        raise ValueError("slot id outside the pool")
+    if len(np.unique(slots)) != len(slots):
+        raise ValueError("slot ids must be distinct")
+    if rope_pos is not None and len(rope_pos) and (np.min(rope_pos) < 0 or np.max(rope_pos) >= rows):
+        raise ValueError("rope position outside the cos/sin table")
+    if k_tok.shape != (len(slots), w.num_kv_heads, w.head_dim) or v_tok.shape != k_tok.shape:
+        raise ValueError("k/v token arrays must be [n, Hkv, D]")
+    params = params_for(w, nb, rows)
+    bf16 = k_tok.dtype == np.uint16
+    dt = torch.int16 if bf16 else torch.float32
+    Hkv, BS, D = w.num_kv_heads, w.block_size, w.head_dim
+    if bf16:
+        fb = int(np.float32(fill).view(np.uint32) >> np.uint32(16))
+        fb = fb - 65536 if fb >= 32768 else fb
+        k_dev = torch.full((nb, Hkv, BS, D), fb, dtype=dt, device=device)
+        v_dev = torch.full((nb, Hkv, D, BS), fb, dtype=dt, device=device)
+    else:
+        k_dev = torch.full((nb, Hkv, BS, D), fill, dtype=dt, device=device)
+        v_dev = torch.full((nb, Hkv, D, BS), fill, dtype=dt, device=device)
+    k = _to_device_bits(k_tok, device)
+    v = _to_device_bits(v_tok, device)
+    sl = torch.from_numpy(np.asarray(slots, np.int64)).to(device)
+    rp = None if rope_pos is None else torch.from_numpy(np.asarray(rope_pos, np.int32)).to(device)
+    cs = None
+    if rope_pos is not None:
+        cs = torch.from_numpy(B.lazy_attn_rope_table(w.rope_base, D, rows)).to(device)
+    B.lazy_attn_store_kv(params, k, v, len(slots), sl, rp, cs, k_dev, v_dev, stream)
+    return k_dev, v_dev
+
+
 def prepare(w, k_dev: torch.Tensor, v_dev: torch.Tensor, device="cuda", split_blocks: int = 0,
-            target_workgroups: int = 0, max_pos: Optional[int] = None) -> DeviceBatch:
+            target_workgroups: int = 0, max_pos: Optional[int] = None,
+            pool_mode="position_free") -> DeviceBatch:
     """Pack and upload everything lazy_attn_decode/prefill need for batch w."""
     rows = int(max_pos) if max_pos is not None else int(w.table_rows())
-    params = B.make_params(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
-                           head_dim=w.head_dim, block_size=w.block_size,
-                           num_blocks=int(k_dev.shape[0]), dtype=w.dtype, scale=w.scale,
-                           max_pos=rows, split_blocks=split_blocks,
-                           target_workgroups=target_workgroups)
+    params = params_for(w, int(k_dev.shape[0]), rows, split_blocks, target_workgroups, pool_mode)
     words, rbs, maxb = B.lazy_attn_pack_segments(params, w.requests)
     table = B.lazy_attn_rope_table(w.rope_base, w.head_dim, rows)
     q = _to_device_bits(w.q, device)

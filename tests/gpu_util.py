@@ -59,12 +59,19 @@ class Device:
         self.k, self.v = upload_pool(src.k_pool, src.v_pool, "cuda")
         torch.cuda.synchronize()
 
-    def run(self, w, split_blocks=0, target_workgroups=0, validate=True, max_pos=None):
+    @classmethod
+    def from_device_pools(cls, k, v):
+        self = cls.__new__(cls)
+        self.k, self.v = k, v
+        return self
+
+    def run(self, w, split_blocks=0, target_workgroups=0, validate=True, max_pos=None,
+            pool_mode="position_free"):
         import torch
         from position_agnostic_kv_lazy_amd import lazy_attn_validate_table
         from position_agnostic_kv_lazy_amd.prepare import prepare
         db = prepare(w, self.k, self.v, split_blocks=split_blocks,
-                     target_workgroups=target_workgroups, max_pos=max_pos)
+                     target_workgroups=target_workgroups, max_pos=max_pos, pool_mode=pool_mode)
         if validate:
             cu = None if w.kind == "decode" else np.asarray(w.cu_q, np.int32)
             lazy_attn_validate_table(db.params, db.batch, db.host_words, db.host_rbs,

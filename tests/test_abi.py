@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -39,7 +39,7 @@ def test_status_strings():
 
 
 def test_params_struct_layout():
-    # int32 x4, int64, int32, float, int32 x3, int32[5] -> 64 bytes, int64 at offset 16
+    # int32 x4, int64, int32, float, int32 x4, int32[4] -> 64 bytes, int64 at offset 16
     assert ctypes.sizeof(B.la_params) == 64
     assert B.la_params.num_blocks.offset == 16
 
@@ -203,3 +203,53 @@ def test_workspace_too_small_rejected_before_launch():
     with pytest.raises(la.LazyAttnError, match="WORKSPACE_TOO_SMALL"):
         la.lazy_attn_decode(p, fake, fake, fake, fake, fake, fake, fake, 64, 324, fake,
                             None, None, None)
+
+
+def test_pack_segments_doc_local_words_carry_segment_start():
+    p = _params(num_blocks=10, max_pos=100, pool_mode="doc_local")
+    segs = [[Segment(3, 20, np.array([4, 2]), False), Segment(60, 5, np.array([9]), False)]]
+    words, rbs, _ = la.lazy_attn_pack_segments(p, segs)
+    ids, pos0, nv, _ = _unpack(words)
+    assert list(ids) == [4, 2, 9] and list(pos0) == [3, 3, 60] and list(nv) == [16, 4, 5]
+    la.lazy_attn_validate_table(p, 1, words, rbs, np.array([70], np.int32))
+
+
+def test_pool_mode_checks():
+    p = _params(pool_mode=2)
+    with pytest.raises(la.LazyAttnError, match="INVALID_ARG.*pool_mode"):
+        la.lazy_attn_decode_workspace_size(p, 4, 10)
+    # doc-local: decode tables may not flag blocks causal; prefill causal
+    # blocks must start blocks of the new-token segment at q_pos0
+    p = _params(num_blocks=10, max_pos=100, pool_mode="doc_local")
+    segs = [[Segment(3, 20, np.array([4, 2]), False), Segment(23, 20, np.array([5, 6]), True)]]
+    words, rbs, _ = la.lazy_attn_pack_segments(p, segs)
+    _, pos0, _, causal = _unpack(words)
+    assert list(pos0) == [3, 3, 23, 39] and list(causal) == [0, 0, 1, 1]
+    with pytest.raises(la.LazyAttnError, match="must not flag"):
+        la.lazy_attn_validate_table(p, 1, words, rbs, np.array([50], np.int32))
+    cu = np.array([0, 20], np.int32)
+    la.lazy_attn_validate_table(p, 1, words, rbs, np.array([23], np.int32), cu)
+    with pytest.raises(la.LazyAttnError, match="new-token segment"):
+        la.lazy_attn_validate_table(p, 1, words, rbs, np.array([24], np.int32), cu)
+
+
+def test_store_kv_argument_checks():
+    p = _params()
+    la.lazy_attn_store_kv(p, None, None, 0, None, None, None, None, None)  # empty: no-op
+    with pytest.raises(la.LazyAttnError, match="n_tokens"):
+        la.lazy_attn_store_kv(p, 1, 1, -1, 1, None, None, 1, 1)
+    with pytest.raises(la.LazyAttnError, match="NULL"):
+        la.lazy_attn_store_kv(p, None, 1, 4, 1, None, None, 1, 1)
+    with pytest.raises(la.LazyAttnError, match="cos_sin"):
+        la.lazy_attn_store_kv(p, 1, 1, 4, 1, 1, None, 1, 1)
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Importing the package before torch must not load a second HIP runtime."""
+    import subprocess
+    import sys
+    code = ("import position_agnostic_kv_lazy_amd, torch\n"
+            "print(sum(1 for l in open('/proc/self/maps') if 'libamdhip64' in l and 'r-xp' in l))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                         check=True).stdout.strip()
+    assert out == "1", out

@@ -1,0 +1,187 @@
+"""Document-local pools and the cache write, on the GPU through the C ABI.
+
+* lazy_attn_store_kv writes keys as given (position-free pool, "LazyAttention"
+  §3.1 "Deferred encoding") or rotated by a caller-chosen position (R_t k with
+  t the index inside the document: each document's cache indexed from
+  position 0, §3.2 "Prefilling"), and values into the dim-major tiles.
+* Decode over a document-local pool rotates q back by the segment start once
+  per segment and reads keys as stored (§3.2 "Decoding", Eq. 6; Example 3.1);
+  prefill rotates each key by its segment start (§3.2 "Prefilling").  Both
+  must give the attention the position-free path gives (the oracle on the raw
+  pool) and what the oracle gives on its own document-local pool.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import rope_theta, run_decode, run_prefill, store_kv
+from position_agnostic_kv_lazy_amd.prepare import store_pool
+from workloads import Segment, build_workload, segment_writes
+
+from gpu_util import Device, assert_lse, assert_parity, config, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _tiny(kind="decode", dtype="bf16", requests=None, Hq=8, Hkv=2, seed=41, q_pos_override=None):
+    if requests is None:
+        requests = ([[("doc", 0), ("doc", 1), ("doc", 2), ("priv", 5)],
+                     [("doc", 3), ("doc", 0), ("doc", 1), ("doc", 0, 300)]] if kind == "decode" else
+                    [[("doc", 0), ("doc", 1), ("new", 40)], [("doc", 3), ("doc", 2), ("new", 70)]])
+    return build_workload(name="docl", kind=kind, dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv,
+                          head_dim=128, block_size=16, rope_base=5e5, doc_lens=[48, 37, 64, 20],
+                          requests=requests, seed=seed, q_pos_override=q_pos_override)
+
+
+def _widen(a):
+    a = a.cpu().numpy()
+    if a.dtype == np.int16:
+        return (a.view(np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return a
+
+
+def _logical(k_dev, v_dev):
+    """Device pools back to the logical [nb, Hkv, BS, D] layout as float64."""
+    return (_widen(k_dev).astype(np.float64),
+            np.swapaxes(_widen(v_dev), -1, -2).astype(np.float64))
+
+
+def _oracle_pools(w, k, v, slots, pos, fill=0.0):
+    base = np.full(w.k_pool.shape, fill)
+    return store_kv(k, v, slots, pos, base, base, block_size=w.block_size,
+                    theta=rope_theta(w.head_dim, w.rope_base))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_store_kv_matches_oracle(dtype, rotate):
+    w = _tiny("decode", dtype)
+    k, v, slots, idx = segment_writes(w, "index")
+    rows = 200000
+    # rotation positions spread over the table (large angles included)
+    pos = ((idx.astype(np.int64) * 7919 + 123) % rows).astype(np.int32) if rotate else None
+    log(f"store_kv {dtype} rotate={rotate}: {len(slots)} tokens")
+    kd, vd = store_pool(w, k, v, slots, pos, max_pos=rows, fill=7.0)
+    torch.cuda.synchronize()
+    kg, vg = _logical(kd, vd)
+    kr, vr = _oracle_pools(w, k, v, slots, pos, fill=7.0)
+    np.testing.assert_array_equal(vg, vr)  # values are copied bit for bit
+    if not rotate:
+        np.testing.assert_array_equal(kg, kr)
+        return
+    written = np.zeros(w.k_pool.shape[:1] + w.k_pool.shape[2:3], bool)
+    written[slots // w.block_size, slots % w.block_size] = True
+    keep = ~written
+    np.testing.assert_array_equal(kg.transpose(0, 2, 1, 3)[keep], 7.0)  # untouched slots
+    err = np.abs(kg - kr)
+    kmax = float(np.max(np.abs(kr)))
+    if dtype == "bf16":  # fp32 rotation rounded once to bf16: half an ulp plus fp32 error
+        bound = 2.0 ** -8 * np.abs(kr) + 2e-6 * kmax
+    else:
+        bound = np.full(kr.shape, 2e-6 * kmax)
+    worst = float(np.max(err - bound))
+    log(f"  store_kv key error max={float(np.max(err)):.3e} (worst margin {worst:.3e})")
+    assert worst <= 0.0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_store_kv_empty_is_noop(dtype):
+    w = _tiny("decode", dtype)
+    k, v, slots, idx = segment_writes(w, "index")
+    kd, vd = store_pool(w, k[:0], v[:0], slots[:0], idx[:0], fill=3.0)
+    torch.cuda.synchronize()
+    kg, vg = _logical(kd, vd)
+    assert np.all(kg == 3.0) and np.all(vg == 3.0)
+
+
+def _doc_local_device(w):
+    k, v, slots, idx = segment_writes(w, "index")
+    kd, vd = store_pool(w, k, v, slots, idx)
+    torch.cuda.synchronize()
+    return Device.from_device_pools(kd, vd), _oracle_pools(w, k, v, slots, idx)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("split_blocks", [0, 2])
+def test_doc_local_decode(dtype, split_blocks):
+    w = _tiny("decode", dtype)
+    log(f"doc-local decode {dtype} split_blocks={split_blocks}")
+    dev, pools = _doc_local_device(w)
+    out, lse, _ = dev.run(w, split_blocks=split_blocks, pool_mode="doc_local")
+    ref = run_decode(w, pools=pools, doc_local=True)
+    ref_pf = run_decode(w)
+    for r in range(w.batch):
+        assert_parity(out[r], ref[r][0], dtype, f"doc-local decode req {r}")
+        assert_lse(lse[r], ref[r][1], dtype, f"doc-local decode req {r}")
+        assert_parity(out[r], ref_pf[r][0], dtype, f"doc-local vs position-free req {r}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_doc_local_decode_segments_after_query(dtype):
+    """Segments placed beyond m: q is rotated by a negative offset m - s."""
+    reqs = [[("doc", 0, 500), ("doc", 1, 10), ("doc", 2, 900)]]
+    w = _tiny("decode", dtype, requests=reqs, q_pos_override=[700])
+    dev, pools = _doc_local_device(w)
+    out, lse, _ = dev.run(w, pool_mode="doc_local")
+    ref = run_decode(w, pools=pools, doc_local=True)
+    assert_parity(out[0], ref[0][0], dtype, "doc-local negative offsets")
+    assert_lse(lse[0], ref[0][1], dtype, "doc-local negative offsets")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_doc_local_prefill(dtype):
+    w = _tiny("prefill", dtype)
+    log(f"doc-local prefill {dtype}")
+    dev, pools = _doc_local_device(w)
+    out, lse, _ = dev.run(w, pool_mode="doc_local")
+    ref = run_prefill(w, pools=pools, doc_local=True)
+    ref_pf = run_prefill(w)
+    for r in range(w.batch):
+        a, b = int(w.cu_q[r]), int(w.cu_q[r + 1])
+        assert_parity(out[a:b], ref[r][0], dtype, f"doc-local prefill req {r}")
+        assert_lse(lse[a:b], ref[r][1], dtype, f"doc-local prefill req {r}")
+        assert_parity(out[a:b], ref_pf[r][0], dtype, f"doc-local vs position-free req {r}")
+
+
+def test_absolute_prerotated_pool_decode():
+    """Keys pre-rotated at absolute positions, every word's start 0 (rotation-off baseline)."""
+    reqs = [[("doc", 0), ("doc", 2), ("priv", 3)], [("doc", 1, 30), ("doc", 3, 200)]]
+    w = _tiny("decode", "bf16", requests=reqs)
+    k, v, slots, pos = segment_writes(w, "absolute")
+    kd, vd = store_pool(w, k, v, slots, pos)
+    import copy
+    w0 = copy.copy(w)
+    w0.requests = [[Segment(0, s.n_tokens, s.blocks, s.is_new) for s in segs]
+                   for segs in w.requests]
+    out, _, _ = Device.from_device_pools(kd, vd).run(w0, pool_mode="doc_local",
+                                                     max_pos=w.table_rows())
+    ref = run_decode(w)
+    for r in range(w.batch):
+        assert_parity(out[r], ref[r][0], "bf16", f"absolute pre-rotated req {r}")
+
+
+def test_doc_local_decode_config2_sampled():
+    """Llama-3-8B decode shapes (config 2, scaled 1/4): shared docs at many offsets."""
+    w = config(2, scale_down=4)
+    log(f"doc-local decode, config 2 shapes /4: batch {w.batch}")
+    dev, pools = _doc_local_device(w)
+    out, lse, _ = dev.run(w, pool_mode="doc_local")
+    reqs = [0, w.batch // 2, w.batch - 1]
+    ref = run_decode(w, requests=reqs, pools=pools, doc_local=True)
+    for r in reqs:
+        assert_parity(out[r], ref[r][0], "bf16", f"cfg2/4 doc-local req {r}")
+        assert_lse(lse[r], ref[r][1], "bf16", f"cfg2/4 doc-local req {r}")
+
+
+def test_doc_local_prefill_config3_sampled():
+    """Llama-3-8B prefill shapes (config 3, scaled 1/8), sampled rows."""
+    w = config(3, scale_down=8)
+    log(f"doc-local prefill, config 3 shapes /8: batch {w.batch}")
+    dev, pools = _doc_local_device(w)
+    out, lse, _ = dev.run(w, pool_mode="doc_local")
+    n0 = w.q_len(0)
+    rows = {0: np.unique(np.clip([0, 1, 31, 32, n0 // 2, n0 - 1], 0, n0 - 1))}
+    ref = run_prefill(w, requests=[0], rows=rows, pools=pools, doc_local=True)
+    a = int(w.cu_q[0])
+    assert_parity(out[a + rows[0]], ref[0][0], "bf16", "cfg3/8 doc-local prefill req 0")
+    assert_lse(lse[a + rows[0]], ref[0][1], "bf16", "cfg3/8 doc-local prefill req 0")

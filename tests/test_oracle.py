@@ -390,3 +390,143 @@ def test_cost_model_printed_percentages():
     assert round(100 * prefill_table_bandwidth(c["N"]), 1) == c["printed_percent"]
     (c,) = g["decode_trigger_overhead"]["cases"]
     assert round(100 * decode_trigger_overhead(c["N"]), 2) == c["printed_percent"]
+
+
+# ------------------------------------------------ document-local pools
+def _doc_local_pools(w):
+    """Write w's segments into a fresh pool pair the document-local way."""
+    from oracle import store_kv
+    from workloads import segment_writes
+    k, v, slots, idx = segment_writes(w, "index")
+    zeros = np.zeros(w.k_pool.shape)
+    return store_kv(k, v, slots, idx, zeros, zeros, block_size=w.block_size,
+                    theta=rope_theta(w.head_dim, w.rope_base))
+
+
+def test_store_kv_copy_rotation_and_untouched_slots():
+    from oracle import store_kv
+    nb, Hkv, BS, D, base = 5, 2, 4, 16, 1e4
+    old_k = RNG.standard_normal((nb, Hkv, BS, D))
+    old_v = RNG.standard_normal((nb, Hkv, BS, D))
+    slots = np.array([3, 17, 8, 9, 0])
+    k = RNG.standard_normal((5, Hkv, D))
+    v = RNG.standard_normal((5, Hkv, D))
+    th = rope_theta(D, base)
+    kp, vp = store_kv(k, v, slots, None, old_k, old_v, block_size=BS, theta=th)
+    pos = np.array([0, 5, 130000, 7, 31])
+    kr, vr = store_kv(k, v, slots, pos, old_k, old_v, block_size=BS, theta=th)
+    touched = np.zeros((nb, BS), bool)
+    for n, s in enumerate(slots):
+        b, t = divmod(int(s), BS)
+        touched[b, t] = True
+        np.testing.assert_array_equal(kp[b, :, t], k[n])
+        np.testing.assert_array_equal(vp[b, :, t], v[n])
+        np.testing.assert_array_equal(vr[b, :, t], v[n])
+        want = _rope_complex(k[n], np.full(Hkv, pos[n], np.float64), base)
+        np.testing.assert_allclose(kr[b, :, t], want, rtol=0, atol=1e-10)
+        np.testing.assert_allclose(np.linalg.norm(kr[b, :, t], axis=-1),
+                                   np.linalg.norm(k[n], axis=-1), rtol=1e-13)
+    keep = ~touched[:, None, :].repeat(Hkv, axis=1)  # [nb, Hkv, BS]
+    np.testing.assert_array_equal(kp[keep], old_k[keep])
+    np.testing.assert_array_equal(vr[keep], old_v[keep])
+
+
+def test_example_3_1_rotate_query_back_by_first_document():
+    """Example 3.1: caches C1, C2 of two documents, both indexed from position 0.
+
+    Reusing C2 right after d1 means rotating the query back by |d1| before it
+    meets C2's keys (C1's keys need no shift).  The brute force below does
+    exactly that with scalar loops; the oracle must agree both on the
+    document-local pool and, through the position-free pool, with keys
+    encoded at their logical positions.
+    """
+    from oracle.brute import brute_rotate
+    D, BS, base, scale = 8, 4, 1e4, 0.3
+    n1, n2 = 5, 7
+    m = n1 + n2 + 2  # the query after both documents
+    raw_k = RNG.standard_normal((n1 + n2, D))
+    raw_v = RNG.standard_normal((n1 + n2, D))
+    q = RNG.standard_normal(D)
+    c1 = [brute_rotate(raw_k[t].tolist(), t, base) for t in range(n1)]       # C1: from 0
+    c2 = [brute_rotate(raw_k[n1 + t].tolist(), t, base) for t in range(n2)]  # C2: from 0
+    scores, vals = [], []
+    q_for_c1 = brute_rotate(q.tolist(), m, base)
+    q_for_c2 = brute_rotate(q.tolist(), m - n1, base)  # rotated back by |d1|
+    for t in range(n1):
+        scores.append(scale * sum(a * b for a, b in zip(q_for_c1, c1[t])))
+        vals.append(raw_v[t])
+    for t in range(n2):
+        scores.append(scale * sum(a * b for a, b in zip(q_for_c2, c2[t])))
+        vals.append(raw_v[n1 + t])
+    mx = max(scores)
+    wts = [math.exp(s - mx) for s in scores]
+    z = sum(wts)
+    want = sum(wt * vv for wt, vv in zip(wts, vals)) / z
+    want_lse = mx + math.log(z)
+
+    # pools: d1 in blocks 0,1; d2 in blocks 2,3 (partial last blocks)
+    nb = 4
+    kp = np.zeros((nb, 1, BS, D))
+    vp = np.zeros((nb, 1, BS, D))
+    for t in range(n1):
+        kp[t // BS, 0, t % BS], vp[t // BS, 0, t % BS] = raw_k[t], raw_v[t]
+    for t in range(n2):
+        kp[2 + t // BS, 0, t % BS], vp[2 + t // BS, 0, t % BS] = raw_k[n1 + t], raw_v[n1 + t]
+    segs = [Segment(0, n1, np.array([0, 1]), False), Segment(n1, n2, np.array([2, 3]), False)]
+    th = rope_theta(D, base)
+    from oracle import store_kv
+    slots = np.array([t for t in range(n1)] + [2 * BS + t for t in range(n2)])
+    idx = np.array(list(range(n1)) + list(range(n2)))
+    kd, vd = store_kv(raw_k[:, None, :], raw_v[:, None, :], slots, idx, np.zeros_like(kp),
+                      np.zeros_like(vp), block_size=BS, theta=th)
+    kw = dict(block_size=BS, num_kv_heads=1, theta=th, scale=scale)
+    o, l = attention_decode(q[None, :], m, segs, kd, vd, doc_local=True, **kw)
+    np.testing.assert_allclose(o[0], want, rtol=0, atol=1e-12)
+    assert abs(l[0] - want_lse) < 1e-12
+    o2, l2 = attention_decode(q[None, :], m, segs, kp, vp, **kw)
+    np.testing.assert_allclose(o2[0], want, rtol=0, atol=1e-12)
+    assert abs(l2[0] - want_lse) < 1e-12
+
+
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_doc_local_pool_equals_position_free(kind):
+    """Same documents at several offsets (one repeated in a request), GQA 2, partial blocks."""
+    w = _tiny(kind, dtype="f32")
+    pools = _doc_local_pools(w)
+    if kind == "decode":
+        a, b = run_decode(w), run_decode(w, pools=pools, doc_local=True)
+    else:
+        a, b = run_prefill(w), run_prefill(w, pools=pools, doc_local=True)
+    for r in a:
+        np.testing.assert_allclose(b[r][0], a[r][0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(b[r][1], a[r][1], rtol=0, atol=1e-12)
+
+
+def test_doc_local_reading_is_not_position_free_reading():
+    """The two pool readings differ on the same bytes (so the flag matters)."""
+    w = _tiny("decode", dtype="f32")
+    pools = _doc_local_pools(w)
+    a = run_decode(w, pools=pools, doc_local=True)
+    b = run_decode(w, pools=pools, doc_local=False)
+    assert max(np.max(np.abs(a[r][0] - b[r][0])) for r in a) > 1e-3
+
+
+def test_absolute_prerotated_pool_is_doc_local_with_zero_starts():
+    """Keys pre-rotated at absolute positions = doc-local pool with every start 0."""
+    from oracle import store_kv
+    from workloads import segment_writes
+    w = _tiny("decode", dtype="f32", requests=[[("doc", 0), ("doc", 2), ("priv", 3)],
+                                               [("doc", 1, 30), ("doc", 3, 50)]])
+    k, v, slots, pos = segment_writes(w, "absolute")
+    zeros = np.zeros(w.k_pool.shape)
+    pools = store_kv(k, v, slots, pos, zeros, zeros, block_size=w.block_size,
+                     theta=rope_theta(w.head_dim, w.rope_base))
+    import copy
+    w0 = copy.copy(w)
+    w0.requests = [[Segment(0, s.n_tokens, s.blocks, s.is_new) for s in segs]
+                   for segs in w.requests]
+    a, b = run_decode(w), run_decode(w0, pools=pools, doc_local=True)
+    for r in a:
+        np.testing.assert_allclose(b[r][0], a[r][0], rtol=0, atol=1e-12)
+    with pytest.raises(ValueError, match="no single absolute"):
+        segment_writes(_tiny("decode", dtype="f32"), "absolute")

@@ -13,6 +13,7 @@ from .synth import (  # noqa: F401
     CONFIGS,
     make_config,
     build_workload,
+    segment_writes,
     zipf_probs,
     f32_to_bf16_bits,
     bf16_bits_to_f32,

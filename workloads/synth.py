@@ -38,6 +38,7 @@ __all__ = [
     "Workload",
     "MixedWorkload",
     "CONFIGS",
+    "segment_writes",
     "make_config",
     "build_workload",
     "zipf_probs",
@@ -445,3 +446,39 @@ def make_config(cfg: int, *, dtype: Optional[str] = None, scale_down: int = 1):
                              shared_pool=(pre.k_pool, pre.v_pool, pre.meta["priv_base"]), **common)
         return MixedWorkload(name="mixed_step", decode=dec, prefill=pre)
     raise ValueError(f"unknown config {cfg}")
+
+
+def segment_writes(w, positions: str = "index"):
+    """Token-level cache-write inputs for the physical segments of w's tables.
+
+    Every distinct block list in w.requests is listed once; its token t (at
+    block blocks[t // BS], slot t % BS) contributes the raw key and value from
+    w's pools, the flat slot id blocks[t // BS] * BS + t % BS and a position
+    index: t itself (positions="index", the in-document index) or the logical
+    position start + t (positions="absolute"; a block list placed at two
+    different starts then has no single absolute position and is rejected).
+    Pure bookkeeping -- no rotation happens here.
+
+    Returns (k [n, Hkv, D], v [n, Hkv, D], slots int64 [n], pos int32 [n]).
+    """
+    BS = w.block_size
+    seen = {}
+    ks, vs, sl, ps = [], [], [], []
+    for segs in w.requests:
+        for seg in segs:
+            key = tuple(int(b) for b in np.asarray(seg.blocks).ravel())
+            if key in seen:
+                if positions == "absolute" and seen[key] != int(seg.start):
+                    raise ValueError(f"blocks {key[:3]}... placed at starts {seen[key]} and "
+                                     f"{int(seg.start)}: no single absolute position")
+                continue
+            seen[key] = int(seg.start)
+            t = np.arange(int(seg.n_tokens))
+            blk = np.asarray(key, np.int64)[t // BS]
+            slot = t % BS
+            ks.append(w.k_pool[blk, :, slot, :])
+            vs.append(w.v_pool[blk, :, slot, :])
+            sl.append(blk * BS + slot)
+            ps.append(t if positions == "index" else int(seg.start) + t)
+    return (np.ascontiguousarray(np.concatenate(ks)), np.ascontiguousarray(np.concatenate(vs)),
+            np.concatenate(sl).astype(np.int64), np.concatenate(ps).astype(np.int32))
