@@ -260,6 +260,96 @@ def _extra_mixed(stream, steps):
         return {"mixed_step": {"error": repr(e)}}
 
 
+def _extra_rotation_ablation(w, k, v, stream, steps, pf_out):
+    """Where deferred RoPE stands against the alternatives, on the headline decode batch.
+
+    * doc_local: each distinct document written once with its keys pre-rotated
+      by the in-document index (lazy_attn_store_kv), then decode in
+      LA_POOL_DOC_LOCAL mode: q rotated once per segment, keys read as stored
+      (the decode design of "LazyAttention" §3.2).
+    * materialised: every request gets a private copy of its segments with keys
+      rotated at their absolute positions (the re-encoding a position-aware
+      cache needs for a document at a new offset), then the same decode with
+      every segment start 0: no key rotation and one q rotation per request --
+      the rotation-off baseline.  The copy itself is timed too: its bytes are
+      the read-modify-write the shared position-free pool never does.
+    All three outputs are compared with the position-free path's output.
+    """
+    import torch
+
+    from position_agnostic_kv_lazy_amd import binding as B
+    from position_agnostic_kv_lazy_amd.prepare import params_for, prepare
+    from workloads import private_copies, segment_slots
+    res = {}
+    BS, D, Hkv = w.block_size, w.head_dim, w.num_kv_heads
+    rows = int(w.table_rows())
+    cs = torch.from_numpy(B.lazy_attn_rope_table(w.rope_base, D, rows)).cuda()
+    pos_free = pf_out.float()
+
+    def gather(slots_np):
+        sl = torch.from_numpy(slots_np).cuda()
+        blk, slot = sl // BS, sl % BS
+        return k[blk, :, slot, :].contiguous(), v[blk, :, :, slot].contiguous()
+
+    def store(params, kt, vt, dst_np, pos_np, kd, vd):
+        dst = torch.from_numpy(dst_np).cuda()
+        pos = torch.from_numpy(pos_np).cuda()
+        return lambda: B.lazy_attn_store_kv(params, kt, vt, len(dst_np), dst, pos, cs, kd, vd,
+                                            stream)
+
+    def decode(wx, kd, vd):
+        db = prepare(wx, kd, vd, pool_mode="doc_local", max_pos=rows)
+        _, ms, _, _ = time_launches(lambda: db.run(stream), steps, 3, stream)
+        torch.cuda.synchronize()
+        diff = float((db.out.view(torch.bfloat16).float() - pos_free).abs().max())
+        return db, ms, diff
+
+    nbytes = w.logical_kv_bytes()
+    # ---- document-local pool
+    slots, idx = segment_slots(w, "index")
+    kt, vt = gather(slots)
+    kd, vd = torch.zeros_like(k), torch.zeros_like(v)
+    p_w = params_for(w, int(k.shape[0]), rows)
+    run_w = store(p_w, kt, vt, slots, idx, kd, vd)
+    _, wms, _, _ = time_launches(run_w, max(3, steps // 4), 1, stream)
+    moved = 4 * len(slots) * Hkv * D * 2
+    _, dms, diff = decode(w, kd, vd)
+    res["doc_local"] = {
+        "decode_event_ms_mean": round(dms, 5),
+        "decode_gbs_logical": round(nbytes / (dms * 1e-3) / 1e9, 1),
+        "write_tokens": int(len(slots)), "write_event_ms_mean": round(wms, 5),
+        "write_gbs": round(moved / (wms * 1e-3) / 1e9, 1),
+        "max_abs_diff_vs_position_free": diff}
+    del kt, vt, kd, vd
+    torch.cuda.empty_cache()
+
+    # ---- materialised per-request copies (rotation-off baseline)
+    reqs, src, dst, pos = private_copies(w)
+    kt, vt = gather(src)
+    nb_m = int(dst.max()) // BS + 1
+    km = torch.zeros((nb_m,) + tuple(k.shape[1:]), dtype=k.dtype, device=k.device)
+    vm = torch.zeros((nb_m,) + tuple(v.shape[1:]), dtype=v.dtype, device=v.device)
+    p_m = params_for(w, nb_m, rows)
+    run_m = store(p_m, kt, vt, dst, pos, km, vm)
+    _, mms, _, _ = time_launches(run_m, max(3, steps // 4), 1, stream)
+    moved = 4 * len(dst) * Hkv * D * 2
+    import copy
+    wm = copy.copy(w)
+    wm.requests = reqs
+    _, rms, diff = decode(wm, km, vm)
+    res["materialised"] = {
+        "decode_event_ms_mean": round(rms, 5),
+        "decode_gbs_logical": round(nbytes / (rms * 1e-3) / 1e9, 1),
+        "copy_tokens": int(len(dst)), "copy_event_ms_mean": round(mms, 5),
+        "copy_gbs": round(moved / (mms * 1e-3) / 1e9, 1),
+        "copy_plus_decode_ms": round(mms + rms, 5),
+        "pool_bytes": int(km.numel() * 2 * 2), "shared_pool_bytes": int(k.numel() * 2 * 2),
+        "max_abs_diff_vs_position_free": diff}
+    del kt, vt, km, vm
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,9 +391,15 @@ def main():
     config = {"workload": wl_name, "batch": w.batch, "q_heads": w.num_q_heads,
               "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
               "docs": "Zipf document mix, shared physical blocks"}
+    ablation = None
     if w.kind == "decode":
         log("timing headline decode")
         main_res = run_decode_workload(w, k, v, stream, args.steps, args.warmup, args.split_blocks)
+        if not args.no_extra:
+            log("rotation ablation: doc-local pool and materialised copies")
+            ablation = _extra_rotation_ablation(w, k, v, stream, max(5, args.steps // 2),
+                                                main_res["_db"].out.view(torch.bfloat16))
+            ablation["position_free_decode_event_ms_mean"] = round(main_res["event_ms_mean"], 5)
         ms = main_res["wall_ms_per_step"]
         value, unit = main_res["logical_kv_bytes"] / (ms * 1e-3) / 1e9, "GB/s"
         config["keys_per_request"] = int(w.keys_per_request()[0])
@@ -334,6 +430,8 @@ def main():
         "roofline": roof,
     }
     extra = {wl_name: _clean(main_res)}
+    if ablation is not None:
+        extra["rotation_ablation"] = ablation
     del main_res, k, v
     torch.cuda.empty_cache()
 

@@ -214,7 +214,8 @@ LA_API la_status lazy_attn_decode_workspace_size(const la_params* p, int32_t bat
  *              (may be NULL when rope_pos is NULL)
  *   k_pool, v_pool  device, layouts above; V is written dim-major
  * Slots must be distinct and < num_blocks * block_size (not checked on the
- * device).  Asynchronous on stream.
+ * device).  k, v, k_pool and v_pool must be 16-byte aligned.  Asynchronous on
+ * stream.
  */
 LA_API la_status lazy_attn_store_kv(const la_params* p, const void* k, const void* v,
                                     int64_t n_tokens, const int64_t* slots,

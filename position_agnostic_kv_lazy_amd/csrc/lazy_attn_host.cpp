@@ -348,6 +348,9 @@ LA_API la_status lazy_attn_store_kv(const la_params* p, const void* k, const voi
       return fail(LA_ERR_INVALID_ARG, "NULL device pointer passed to lazy_attn_store_kv");
     if (rope_pos && !cos_sin)
       return fail(LA_ERR_INVALID_ARG, "rope_pos given without cos_sin");
+    for (const void* ptr : {k, v, static_cast<const void*>(k_pool), static_cast<const void*>(v_pool)})
+      if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+        return fail(LA_ERR_INVALID_ARG, "k, v, k_pool and v_pool must be 16-byte aligned");
     const hipError_t e = lazyattn::launch_store_kv(
         k, v, n_tokens, slots, rope_pos, cos_sin, p->num_kv_heads, p->head_dim, p->block_size,
         p->dtype == LA_BF16, k_pool, v_pool, static_cast<hipStream_t>(stream));

@@ -241,7 +241,9 @@ def test_store_kv_argument_checks():
     with pytest.raises(la.LazyAttnError, match="NULL"):
         la.lazy_attn_store_kv(p, None, 1, 4, 1, None, None, 1, 1)
     with pytest.raises(la.LazyAttnError, match="cos_sin"):
-        la.lazy_attn_store_kv(p, 1, 1, 4, 1, 1, None, 1, 1)
+        la.lazy_attn_store_kv(p, 16, 16, 4, 16, 16, None, 16, 16)
+    with pytest.raises(la.LazyAttnError, match="aligned"):
+        la.lazy_attn_store_kv(p, 16, 18, 4, 16, None, None, 16, 16)
 
 
 def test_one_hip_runtime_whatever_the_import_order():

@@ -84,6 +84,27 @@ def test_store_kv_matches_oracle(dtype, rotate):
     assert worst <= 0.0
 
 
+@pytest.mark.parametrize("order", ["whole_blocks", "shuffled", "reversed"])
+def test_store_kv_slot_orders(order):
+    """Whole in-order blocks take the vector path; any other order the per-element one."""
+    reqs = [[("doc", 0), ("doc", 1), ("doc", 2), ("doc", 3)]]
+    w = build_workload(name="st", kind="decode", dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16, rope_base=5e5, doc_lens=[48, 64, 32, 16],
+                       requests=reqs, seed=5)
+    k, v, slots, idx = segment_writes(w, "index")
+    if order != "whole_blocks":
+        perm = (np.random.default_rng(3).permutation(len(slots)) if order == "shuffled"
+                else np.arange(len(slots))[::-1])
+        k, v, slots, idx = k[perm], v[perm], slots[perm], idx[perm]
+    log(f"store_kv slot order {order}")
+    kd, vd = store_pool(w, k, v, slots, None, fill=-2.0)
+    torch.cuda.synchronize()
+    kg, vg = _logical(kd, vd)
+    kr, vr = _oracle_pools(w, k, v, slots, None, fill=-2.0)
+    np.testing.assert_array_equal(kg, kr)
+    np.testing.assert_array_equal(vg, vr)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_store_kv_empty_is_noop(dtype):
     w = _tiny("decode", dtype)

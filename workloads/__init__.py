@@ -14,6 +14,8 @@ from .synth import (  # noqa: F401
     make_config,
     build_workload,
     segment_writes,
+    segment_slots,
+    private_copies,
     zipf_probs,
     f32_to_bf16_bits,
     bf16_bits_to_f32,

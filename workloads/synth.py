@@ -39,6 +39,8 @@ __all__ = [
     "MixedWorkload",
     "CONFIGS",
     "segment_writes",
+    "segment_slots",
+    "private_copies",
     "make_config",
     "build_workload",
     "zipf_probs",
@@ -446,6 +448,57 @@ def make_config(cfg: int, *, dtype: Optional[str] = None, scale_down: int = 1):
                              shared_pool=(pre.k_pool, pre.v_pool, pre.meta["priv_base"]), **common)
         return MixedWorkload(name="mixed_step", decode=dec, prefill=pre)
     raise ValueError(f"unknown config {cfg}")
+
+
+def segment_slots(w, positions: str = "index"):
+    """Flat slot ids and position indices of every distinct segment (see segment_writes)."""
+    BS = w.block_size
+    seen = {}
+    sl, ps = [], []
+    for segs in w.requests:
+        for seg in segs:
+            key = tuple(int(b) for b in np.asarray(seg.blocks).ravel())
+            if key in seen:
+                if positions == "absolute" and seen[key] != int(seg.start):
+                    raise ValueError(f"blocks {key[:3]}... placed at starts {seen[key]} and "
+                                     f"{int(seg.start)}: no single absolute position")
+                continue
+            seen[key] = int(seg.start)
+            t = np.arange(int(seg.n_tokens))
+            blk = np.asarray(key, np.int64)[t // BS]
+            sl.append(blk * BS + t % BS)
+            ps.append(t if positions == "index" else int(seg.start) + t)
+    return np.concatenate(sl).astype(np.int64), np.concatenate(ps).astype(np.int32)
+
+
+def private_copies(w):
+    """Per-request private copies of every segment, as a materialising cache would hold them.
+
+    Request r's segments are laid out in fresh blocks of a new pool (numbered
+    from 0), each at its own logical positions.  Returns (requests, src_slots,
+    dst_slots, positions): the new segment lists (with start 0, for a pool
+    whose keys are pre-rotated at absolute positions), and per token the
+    source slot in w's pool, the destination slot and the logical position.
+    Pure bookkeeping.
+    """
+    BS = w.block_size
+    nxt = 0
+    reqs, src, dst, pos = [], [], [], []
+    for segs in w.requests:
+        out = []
+        for seg in segs:
+            n = int(seg.n_tokens)
+            nb = (n + BS - 1) // BS
+            blocks = np.arange(nxt, nxt + nb, dtype=np.int64)
+            nxt += nb
+            t = np.arange(n)
+            src.append(np.asarray(seg.blocks, np.int64)[t // BS] * BS + t % BS)
+            dst.append(blocks[t // BS] * BS + t % BS)
+            pos.append(int(seg.start) + t)
+            out.append(Segment(0, n, blocks, seg.is_new))
+        reqs.append(out)
+    return (reqs, np.concatenate(src).astype(np.int64), np.concatenate(dst).astype(np.int64),
+            np.concatenate(pos).astype(np.int32))
 
 
 def segment_writes(w, positions: str = "index"):
