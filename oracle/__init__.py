@@ -17,6 +17,7 @@ rest on the definition of RoPE attention itself.
 from .lazy_oracle import (  # noqa: F401
     rope_theta,
     rope_rotate,
+    alibi_slopes,
     gather_request,
     attention_decode,
     attention_prefill,

@@ -13,37 +13,46 @@ import math
 __all__ = ["brute_attention", "brute_rotate"]
 
 
-def brute_rotate(vec, pos, base):
-    """Rotate one vector (list) to position pos: pair (i, i + D/2) by pos * base^(-2i/D)."""
+def brute_rotate(vec, pos, base, interleaved=False):
+    """Rotate one vector (list) to position pos.
+
+    Pair i -- (i, i + D/2), or (2i, 2i + 1) when interleaved -- turns by
+    pos * base^(-2i/D).
+    """
     D = len(vec)
     h = D // 2
     out = [0.0] * D
     for i in range(h):
         ang = pos * (base ** (-2.0 * i / D))
         c, s = math.cos(ang), math.sin(ang)
-        out[i] = vec[i] * c - vec[i + h] * s
-        out[i + h] = vec[i] * s + vec[i + h] * c
+        a, b = (2 * i, 2 * i + 1) if interleaved else (i, i + h)
+        out[a] = vec[a] * c - vec[b] * s
+        out[b] = vec[a] * s + vec[b] * c
     return out
 
 
-def brute_attention(queries, keys, scale, base):
+def brute_attention(queries, keys, scale, base, interleaved=False, alibi_slope=None):
     """queries: list of (qvec, qpos); keys: list of (kvec, vvec, kpos, causal).
 
-    A key marked causal is visible to a query only when kpos <= qpos.
-    Returns list of (out vector, lse) per query.
+    A key marked causal is visible to a query only when kpos <= qpos.  With
+    alibi_slope set, no rotation is applied and slope * (kpos - qpos) is added
+    to each score.  Returns list of (out vector, lse) per query.
     """
     res = []
     for qv, qp in queries:
-        qr = brute_rotate(qv, qp, base)
+        qr = qv if alibi_slope is not None else brute_rotate(qv, qp, base, interleaved)
         scores, vals = [], []
         for kv, vv, kp, causal in keys:
             if causal and kp > qp:
                 continue
-            kr = brute_rotate(kv, kp, base)
+            kr = kv if alibi_slope is not None else brute_rotate(kv, kp, base, interleaved)
             dot = 0.0
             for a, b in zip(qr, kr):
                 dot += a * b
-            scores.append(scale * dot)
+            sc = scale * dot
+            if alibi_slope is not None:
+                sc += alibi_slope * (kp - qp)
+            scores.append(sc)
             vals.append(vv)
         mx = max(scores)
         ws = [math.exp(s - mx) for s in scores]

@@ -36,6 +36,7 @@ import numpy as np
 __all__ = [
     "rope_theta",
     "rope_rotate",
+    "alibi_slopes",
     "gather_request",
     "attention_decode",
     "attention_prefill",
@@ -64,25 +65,53 @@ def rope_theta(head_dim: int, base: float) -> np.ndarray:
     return np.power(float(base), -2.0 * i / float(head_dim))
 
 
-def rope_rotate(x, pos, theta) -> np.ndarray:
+def rope_rotate(x, pos, theta, pairing: str = "half") -> np.ndarray:
     """Rotate x[..., D] to position(s) pos (broadcast over leading axes).
 
-    Pair (i, i+D/2) is rotated by angle pos*theta_i:
+    pairing="half": pair (i, i+D/2) is rotated by angle pos*theta_i:
       y_i = x_i cos - x_{i+D/2} sin,   y_{i+D/2} = x_i sin + x_{i+D/2} cos
     (§3.2 "Prefilling", the relative-rotation formula with the offset taken
-    as the absolute position).
+    as the absolute position).  pairing="interleaved": the same rotation on
+    the adjacent pair (2i, 2i+1), the interleaved RoPE of §3.5.
 
-    Pins: equals multiplication of x_i + j x_{i+D/2} by exp(j pos theta_i)
-    (RoPE's complex form, computed with numpy complex arithmetic); Fact 3.2
-    (R_m q).(R_n k) = q.R_{n-m} k; norm preservation; rot(x, 0) = x.
+    Pins: equals multiplication of x_i + j x_{i+D/2} (interleaved:
+    x_{2i} + j x_{2i+1}) by exp(j pos theta_i) (RoPE's complex form, computed
+    with numpy complex arithmetic); Fact 3.2 (R_m q).(R_n k) = q.R_{n-m} k;
+    norm preservation; rot(x, 0) = x.
     """
     x = np.asarray(x, dtype=np.float64)
     pos = np.asarray(pos, dtype=np.float64)
-    half = x.shape[-1] // 2
     ang = pos[..., None] * np.asarray(theta, dtype=np.float64)
     c, s = np.cos(ang), np.sin(ang)
+    if pairing == "interleaved":
+        x1, x2 = x[..., 0::2], x[..., 1::2]
+        y = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (x.shape[-1],)))
+        y[..., 0::2] = x1 * c - x2 * s
+        y[..., 1::2] = x1 * s + x2 * c
+        return y
+    if pairing != "half":
+        raise ValueError(f"unknown pairing {pairing!r}")
+    half = x.shape[-1] // 2
     x1, x2 = x[..., :half], x[..., half:]
     return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def alibi_slopes(num_heads: int) -> np.ndarray:
+    """ALiBi head slopes (the score-space method of §3.5, published rule).
+
+    For n a power of two the slopes are the geometric sequence
+    2^(-8/n), 2^(-16/n), ..., 2^(-8); otherwise the n' = 2^floor(log2 n)
+    sequence is followed by every other slope of the 2n' sequence.
+    Pins: n = 8 gives 1/2, 1/4, ..., 1/256; the first values for n = 12.
+    """
+    def pow2(n):
+        start = 2.0 ** (-8.0 / n)
+        return [start ** (i + 1) for i in range(n)]
+    n = int(num_heads)
+    p = 1 << (n.bit_length() - 1)
+    if p == n:
+        return np.array(pow2(n))
+    return np.array(pow2(p) + pow2(2 * p)[0::2][: n - p])
 
 
 def gather_request(k_pool, v_pool, segments, block_size: int, kv_head: int):
@@ -117,18 +146,18 @@ def _segment_starts(segments) -> np.ndarray:
     return np.concatenate(parts) if parts else np.zeros(0, np.int64)
 
 
-def _encode_keys(K, pos, segments, theta, doc_local):
+def _encode_keys(K, pos, segments, theta, doc_local, pairing="half"):
     """Keys encoded at their logical positions.
 
     Position-free pool: R_p k.  Document-local pool (stored R_t k): R_s of the
     stored key, s = the segment's start, which is R_{s+t} k.
     """
     if doc_local:
-        return rope_rotate(K, _segment_starts(segments), theta)
-    return rope_rotate(K, pos, theta)
+        return rope_rotate(K, _segment_starts(segments), theta, pairing)
+    return rope_rotate(K, pos, theta, pairing)
 
 
-def store_kv(k, v, slots, rope_pos, k_pool, v_pool, *, block_size, theta):
+def store_kv(k, v, slots, rope_pos, k_pool, v_pool, *, block_size, theta, pairing="half"):
     """The cache write: new tokens' keys and values into pool slots.
 
     Token n goes to block slots[n] // BS, slot slots[n] % BS; its key is
@@ -136,7 +165,10 @@ def store_kv(k, v, slots, rope_pos, k_pool, v_pool, *, block_size, theta):
     encoding") or rotated to rope_pos[n] (R_p k; p = the index inside its
     document for a document-local pool, §3.2 "Prefilling"), its value as
     given.  Returns float64 copies of the logical [nb, Hkv, BS, D] pools;
-    slots not listed keep their old contents.
+    slots not listed keep their old contents.  With interleaved pairing the
+    key is rotated on pairs (2i, 2i+1) and then stored with its dimensions in
+    the order (even dims, odd dims) -- the storage order of such pools, which
+    turns each pair back into (i, i + D/2).
 
     Pins: rope_pos None is an exact copy; a rotated key equals the complex
     product x * exp(j p theta) and keeps its norm; Example 3.1 through
@@ -148,7 +180,9 @@ def store_kv(k, v, slots, rope_pos, k_pool, v_pool, *, block_size, theta):
     slots = np.asarray(slots, np.int64)
     blk, sl = slots // block_size, slots % block_size
     if rope_pos is not None:
-        kf = rope_rotate(kf, np.asarray(rope_pos, np.int64)[:, None], theta)
+        kf = rope_rotate(kf, np.asarray(rope_pos, np.int64)[:, None], theta, pairing)
+    if pairing == "interleaved":
+        kf = np.concatenate([kf[..., 0::2], kf[..., 1::2]], axis=-1)
     kp[blk, :, sl, :] = kf
     vp[blk, :, sl, :] = vf
     return kp, vp
@@ -169,14 +203,19 @@ def _softmax_attend(scores: np.ndarray, V: np.ndarray):
 
 
 def attention_decode(q, q_pos, segments, k_pool, v_pool, *, block_size, num_kv_heads,
-                     theta, scale, rotate=True, doc_local=False):
+                     theta, scale, rotate=True, doc_local=False, pairing="half",
+                     alibi=None):
     """One decode query (all heads) of one request, eager RoPE.
 
     q: [Hq, D]; q_pos: the query's logical position m.  Keys are gathered,
     re-encoded at their positions (the materialised cache the method avoids)
     and attended with textbook softmax.  Returns out [Hq, D], lse [Hq].
     rotate=False drops RoPE entirely (used by the identity-table pin);
-    doc_local=True reads a document-local pool (stored keys R_t k).
+    doc_local=True reads a document-local pool (stored keys R_t k);
+    pairing selects the RoPE pairs (see rope_rotate).  alibi, an array of Hq
+    slopes, replaces RoPE by the ALiBi score bias slope_h * (p - m) (§3.5
+    "Score-space positional methods"; -slope times the distance for keys at
+    or before the query).
     """
     qf = _as_f64(q)
     Hq, D = qf.shape
@@ -186,12 +225,15 @@ def attention_decode(q, q_pos, segments, k_pool, v_pool, *, block_size, num_kv_h
     for g in range(num_kv_heads):
         K, V, pos, _ = gather_request(k_pool, v_pool, segments, block_size, g)
         qs = qf[g * G:(g + 1) * G]
-        if rotate:
-            Kt = _encode_keys(K, pos, segments, theta, doc_local)
-            qt = rope_rotate(qs, np.full(G, q_pos), theta)
+        if rotate and alibi is None:
+            Kt = _encode_keys(K, pos, segments, theta, doc_local, pairing)
+            qt = rope_rotate(qs, np.full(G, q_pos), theta, pairing)
         else:
             Kt, qt = K, qs
         s = scale * (qt @ Kt.T)
+        if alibi is not None:
+            sl = np.asarray(alibi, np.float64)[g * G:(g + 1) * G]
+            s = s + sl[:, None] * (pos[None, :] - float(q_pos))
         o, l = _softmax_attend(s, V)
         out[g * G:(g + 1) * G] = o
         lse[g * G:(g + 1) * G] = l
@@ -222,14 +264,16 @@ def attention_decode_relative(q, q_pos, segments, k_pool, v_pool, *, block_size,
 
 
 def attention_prefill(q, q_pos0, segments, k_pool, v_pool, *, block_size, num_kv_heads,
-                      theta, scale, rotate=True, rows=None, doc_local=False):
+                      theta, scale, rotate=True, rows=None, doc_local=False, pairing="half",
+                      alibi=None):
     """New-token attention of one request, eager RoPE.
 
     q: [T, Hq, D]; new token j sits at position q_pos0 + j.  Keys of cached
     segments are all visible; keys of the new-token segment are visible iff
     their position is <= the query's.  rows optionally restricts the query
     rows computed (sampled parity).  Returns out [T', Hq, D], lse [T', Hq].
-    doc_local=True reads a document-local pool (stored keys R_t k).
+    doc_local=True reads a document-local pool (stored keys R_t k);
+    pairing and alibi as for attention_decode.
     """
     qf = _as_f64(q)
     T, Hq, D = qf.shape
@@ -240,13 +284,16 @@ def attention_prefill(q, q_pos0, segments, k_pool, v_pool, *, block_size, num_kv
     lse = np.empty((len(rows), Hq))
     for g in range(num_kv_heads):
         K, V, pos, new = gather_request(k_pool, v_pool, segments, block_size, g)
-        Kt = _encode_keys(K, pos, segments, theta, doc_local) if rotate else K
+        use_rope = rotate and alibi is None
+        Kt = _encode_keys(K, pos, segments, theta, doc_local, pairing) if use_rope else K
         visible = (~new)[None, :] | (pos[None, :] <= qpos[:, None])  # [T', n]
         for hh in range(G):
             h = g * G + hh
             qs = qf[rows, h, :]
-            qt = rope_rotate(qs, qpos, theta) if rotate else qs
+            qt = rope_rotate(qs, qpos, theta, pairing) if use_rope else qs
             s = scale * (qt @ Kt.T)
+            if alibi is not None:
+                s = s + float(alibi[h]) * (pos[None, :] - qpos[:, None])
             s = np.where(visible, s, -np.inf)
             o, l = _softmax_attend(s, V)
             out[:, h, :] = o
@@ -258,11 +305,13 @@ def _theta_of(w):
     return rope_theta(w.head_dim, w.rope_base)
 
 
-def run_decode(w, requests=None, rotate=True, pools=None, doc_local=False):
+def run_decode(w, requests=None, rotate=True, pools=None, doc_local=False, pairing="half",
+               alibi=None):
     """Oracle outputs for decode workload w: {r: (out [Hq, D], lse [Hq])}.
 
     pools, if given, replaces (w.k_pool, w.v_pool), e.g. by a document-local
-    pool written with store_kv (then doc_local=True).
+    pool written with store_kv (then doc_local=True).  pairing / alibi select
+    the positional encoding (see attention_decode).
     """
     th = _theta_of(w)
     kp, vp = (w.k_pool, w.v_pool) if pools is None else pools
@@ -271,15 +320,17 @@ def run_decode(w, requests=None, rotate=True, pools=None, doc_local=False):
     for r in reqs:
         res[r] = attention_decode(w.q[r], int(w.q_pos[r]), w.requests[r], kp, vp,
                                   block_size=w.block_size, num_kv_heads=w.num_kv_heads,
-                                  theta=th, scale=w.scale, rotate=rotate, doc_local=doc_local)
+                                  theta=th, scale=w.scale, rotate=rotate, doc_local=doc_local,
+                                  pairing=pairing, alibi=alibi)
     return res
 
 
-def run_prefill(w, requests=None, rows=None, rotate=True, pools=None, doc_local=False):
+def run_prefill(w, requests=None, rows=None, rotate=True, pools=None, doc_local=False,
+                pairing="half", alibi=None):
     """Oracle outputs for prefill workload w: {r: (out [T', Hq, D], lse [T', Hq])}.
 
     rows, if given, maps request -> array of new-token indices to compute;
-    pools / doc_local as for run_decode.
+    pools / doc_local / pairing / alibi as for run_decode.
     """
     th = _theta_of(w)
     kp, vp = (w.k_pool, w.v_pool) if pools is None else pools
@@ -291,5 +342,5 @@ def run_prefill(w, requests=None, rows=None, rotate=True, pools=None, doc_local=
         res[r] = attention_prefill(w.q[a:b], int(w.q_pos[r]), w.requests[r], kp, vp,
                                    block_size=w.block_size, num_kv_heads=w.num_kv_heads,
                                    theta=th, scale=w.scale, rotate=rotate, rows=rr,
-                                   doc_local=doc_local)
+                                   doc_local=doc_local, pairing=pairing, alibi=alibi)
     return res

@@ -530,3 +530,129 @@ def test_absolute_prerotated_pool_is_doc_local_with_zero_starts():
         np.testing.assert_allclose(b[r][0], a[r][0], rtol=0, atol=1e-12)
     with pytest.raises(ValueError, match="no single absolute"):
         segment_writes(_tiny("decode", dtype="f32"), "absolute")
+
+
+# ------------------------------------------------ interleaved RoPE pairing
+def test_interleaved_rotation_is_complex_multiplication():
+    D, base = 32, 1e4
+    th = rope_theta(D, base)
+    x = RNG.standard_normal((5, D))
+    pos = np.array([0, 1, 17, 4096, 131071])
+    inv = 1.0 / (base ** (np.arange(0, D, 2, dtype=np.float64) / D))
+    z = (x[:, 0::2] + 1j * x[:, 1::2]) * np.exp(1j * pos[:, None] * inv[None, :])
+    want = np.empty_like(x)
+    want[:, 0::2], want[:, 1::2] = z.real, z.imag
+    np.testing.assert_allclose(rope_rotate(x, pos, th, "interleaved"), want, rtol=0, atol=1e-10)
+
+
+def test_interleaved_fact_3_2():
+    D = 64
+    th = rope_theta(D, 5e5)
+    q, k = RNG.standard_normal(D), RNG.standard_normal(D)
+    for m, n in [(0, 5), (700, 3), (65536, 131071)]:
+        lhs = rope_rotate(q, m, th, "interleaved") @ rope_rotate(k, n, th, "interleaved")
+        rhs = q @ rope_rotate(k, n - m, th, "interleaved")
+        assert abs(lhs - rhs) < 1e-10
+
+
+def _deinterleaved(w):
+    """Copy of w with q and K stored in (even dims, odd dims) order."""
+    import copy
+    w2 = copy.copy(w)
+    perm = np.concatenate([np.arange(0, w.head_dim, 2), np.arange(1, w.head_dim, 2)])
+    w2.q = w.q[..., perm]
+    w2.k_pool = w.k_pool[..., perm]
+    return w2
+
+
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_interleaved_equals_half_split_on_permuted_dims(kind):
+    """Interleaved pairs of (q, k) are the half-split pairs of the permuted vectors."""
+    w = _tiny(kind, dtype="f32")
+    run = run_decode if kind == "decode" else run_prefill
+    a = run(w, pairing="interleaved")
+    b = run(_deinterleaved(w))
+    for r in a:
+        np.testing.assert_allclose(a[r][0], b[r][0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(a[r][1], b[r][1], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_brute_force_interleaved_and_alibi(kind):
+    from oracle import alibi_slopes
+    w = _tiny(kind, dtype="f32")
+    sl = alibi_slopes(w.num_q_heads)
+    run = run_decode if kind == "decode" else run_prefill
+    inter = run(w, pairing="interleaved")
+    ali = run(w, alibi=sl)
+    for r in range(w.batch):
+        for h in range(w.num_q_heads):
+            g = h // w.group
+            keys = []
+            for s in w.requests[r]:
+                for t in range(s.n_tokens):
+                    b = int(s.blocks[t // w.block_size])
+                    keys.append((w.values_f32(w.k_pool[b, g, t % w.block_size]).tolist(),
+                                 w.values_f32(w.v_pool[b, g, t % w.block_size]).tolist(),
+                                 s.start + t, s.is_new))
+            if kind == "decode":
+                qs = [(w.values_f32(w.q[r, h]).tolist(), int(w.q_pos[r]))]
+            else:
+                a0 = int(w.cu_q[r])
+                qs = [(w.values_f32(w.q[a0 + j, h]).tolist(), int(w.q_pos[r]) + j)
+                      for j in range(w.q_len(r))]
+            bi = brute_attention(qs, keys, w.scale, w.rope_base, interleaved=True)
+            ba = brute_attention(qs, keys, w.scale, w.rope_base, alibi_slope=float(sl[h]))
+            for j, (o, l) in enumerate(bi):
+                oi = inter[r][0][h] if kind == "decode" else inter[r][0][j, h]
+                np.testing.assert_allclose(oi, o, rtol=0, atol=1e-12)
+            for j, (o, l) in enumerate(ba):
+                oa = ali[r][0][h] if kind == "decode" else ali[r][0][j, h]
+                la = ali[r][1][h] if kind == "decode" else ali[r][1][j, h]
+                np.testing.assert_allclose(oa, o, rtol=0, atol=1e-12)
+                assert abs(la - l) < 1e-12
+
+
+# ------------------------------------------------------------------ ALiBi
+def test_alibi_slopes_published_values():
+    from oracle import alibi_slopes
+    np.testing.assert_allclose(alibi_slopes(8), [2.0 ** -k for k in range(1, 9)], rtol=1e-15)
+    want12 = [2.0 ** -k for k in range(1, 9)] + [2.0 ** -0.5, 2.0 ** -1.5, 2.0 ** -2.5,
+                                                  2.0 ** -3.5]
+    np.testing.assert_allclose(alibi_slopes(12), want12, rtol=1e-15)
+    np.testing.assert_allclose(alibi_slopes(1), [2.0 ** -8], rtol=1e-15)
+
+
+def test_alibi_closed_form_two_equal_keys():
+    """Equal q.k: weights follow exp(slope * (p - m)) alone."""
+    D, s_, m = 8, 0.25, 40
+    k = RNG.standard_normal(D)
+    v = RNG.standard_normal((2, D))
+    kp = np.zeros((2, 1, 4, D))
+    vp = np.zeros((2, 1, 4, D))
+    kp[0, 0, 0], kp[1, 0, 0] = k, k
+    vp[0, 0, 0], vp[1, 0, 0] = v[0], v[1]
+    segs = [Segment(30, 1, np.array([0]), False), Segment(37, 1, np.array([1]), False)]
+    q = RNG.standard_normal((1, D))
+    o, _ = attention_decode(q, m, segs, kp, vp, block_size=4, num_kv_heads=1,
+                            theta=rope_theta(D, 1e4), scale=0.5, alibi=np.array([s_]))
+    w1, w2 = math.exp(s_ * (30 - m)), math.exp(s_ * (37 - m))
+    np.testing.assert_allclose(o[0], (w1 * v[0] + w2 * v[1]) / (w1 + w2), rtol=0, atol=1e-13)
+
+
+def test_alibi_zero_slopes_is_unrotated_attention_and_shift_invariant():
+    w = _tiny("decode", dtype="f32")
+    a = run_decode(w, alibi=np.zeros(w.num_q_heads))
+    b = run_decode(w, rotate=False)
+    for r in a:
+        np.testing.assert_allclose(a[r][0], b[r][0], rtol=0, atol=1e-13)
+    from oracle import alibi_slopes
+    sl = alibi_slopes(w.num_q_heads)
+    c = run_decode(w, alibi=sl)
+    import copy
+    w2 = copy.copy(w)
+    w2.requests = [_shifted(segs, 1000) for segs in w.requests]
+    w2.q_pos = w.q_pos + 1000
+    d = run_decode(w2, alibi=sl)
+    for r in c:
+        np.testing.assert_allclose(c[r][0], d[r][0], rtol=0, atol=1e-11)
