@@ -113,6 +113,30 @@ typedef enum la_dtype { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
  */
 typedef enum la_pool_mode { LA_POOL_POSITION_FREE = 0, LA_POOL_DOC_LOCAL = 1 } la_pool_mode;
 
+/*
+ * Positional encoding applied inside the kernels (§3.5 "Generalization Beyond
+ * Standard RoPE": the score stays q^T R_{n-m} k for RoPE-family variants, or
+ * gets a position-dependent bias for score-space methods).
+ *  LA_ROPE_HALF (default): RoPE on feature pairs (i, i + D/2).
+ *  LA_ROPE_INTERLEAVED: RoPE on adjacent pairs (2i, 2i + 1) of q and k.
+ *    lazy_attn_store_kv stores such keys with their dimensions reordered to
+ *    (even dims, odd dims), which turns every pair into (i, i + D/2); k_pool
+ *    then holds keys in that order (write it with lazy_attn_store_kv, or apply
+ *    the same reordering).  q, v and out keep the model's order.
+ *  LA_ALIBI: no rotation; the score of a key at position p for a query at m
+ *    gets slope_h * (p - m) (-slope_h times the distance for keys at or
+ *    before the query).  The cos_sin argument of decode/prefill then points
+ *    to the per-query-head slopes, float32 [num_q_heads]
+ *    (lazy_attn_alibi_slopes gives the standard ones).  Position-free pools
+ *    only.
+ * Scaled / NTK / YaRN RoPE variants change only the cos/sin table.
+ */
+typedef enum la_pos_encoding {
+  LA_ROPE_HALF = 0,
+  LA_ROPE_INTERLEAVED = 1,
+  LA_ALIBI = 2
+} la_pos_encoding;
+
 /* Packing limits of the 64-bit block word. */
 #define LA_MAX_POSITION ((int64_t)1 << 24) /* positions must be < 2^24 */
 #define LA_MAX_BLOCK_ID ((int64_t)1 << 32)
@@ -129,7 +153,8 @@ typedef struct la_params {
   int32_t split_blocks;  /* decode: blocks per split group, 0 = automatic */
   int32_t target_workgroups; /* decode split heuristic, 0 = 1024 (256 CUs x 4) */
   int32_t pool_mode;     /* la_pool_mode of k_pool (above) */
-  int32_t reserved[4];   /* must be zero */
+  int32_t pos_encoding;  /* la_pos_encoding (above) */
+  int32_t reserved[3];   /* must be zero */
 } la_params;
 
 /* Human-readable name of a status code (static string). */
@@ -149,6 +174,14 @@ LA_API const char* lazy_attn_last_error(void);
  *   out       host, rows * head_dim floats
  */
 LA_API la_status lazy_attn_rope_table(double base, int32_t head_dim, int32_t rows, float* out);
+
+/*
+ * Standard ALiBi slopes for num_heads heads (host): 2^(-8/n), 2^(-16/n), ...
+ * for n a power of two; otherwise the nearest lower power of two's sequence
+ * followed by every other slope of the next power of two's sequence.
+ *   out  host, num_heads floats
+ */
+LA_API la_status lazy_attn_alibi_slopes(int32_t num_heads, float* out);
 
 /*
  * Pack per-request segment lists into block words (host only).
@@ -203,7 +236,9 @@ LA_API la_status lazy_attn_decode_workspace_size(const la_params* p, int32_t bat
 
 /*
  * Write n_tokens keys and values into pool slots (the cache write that
- * precedes attention; keys are stored once and never re-encoded).
+ * precedes attention; keys are stored once and never re-encoded).  With
+ * LA_ROPE_INTERLEAVED keys are rotated on pairs (2i, 2i + 1) and stored in
+ * (even dims, odd dims) order.
  *   k, v       device [n_tokens][num_kv_heads][head_dim], pool dtype
  *   slots      device int64 [n_tokens]: block_id * block_size + slot
  *   rope_pos   device int32 [n_tokens] or NULL.  NULL stores keys as given
@@ -229,7 +264,8 @@ LA_API la_status lazy_attn_store_kv(const la_params* p, const void* k, const voi
  *   k_pool/v_pool  device, layouts above
  *   blk_words      device packed words; req_blk_start device [batch+1]
  *   q_pos          device [batch] logical position m of each query
- *   cos_sin        device [max_pos][2][D/2] float32
+ *   cos_sin        device [max_pos][2][D/2] float32 (LA_ALIBI: the slopes,
+ *                  float32 [num_q_heads])
  *   max_blocks_per_req  host scalar: upper bound of per-request block counts
  *   out            device [batch][Hq][D] (same dtype as q)
  *   lse            device [batch][Hq] float32 or NULL

@@ -11,12 +11,16 @@ from .binding import (  # noqa: F401
     LA_FP32,
     LA_POOL_POSITION_FREE,
     LA_POOL_DOC_LOCAL,
+    LA_ROPE_HALF,
+    LA_ROPE_INTERLEAVED,
+    LA_ALIBI,
     LazyAttnError,
     la_params,
     make_params,
     lazy_attn_status_string,
     lazy_attn_last_error,
     lazy_attn_rope_table,
+    lazy_attn_alibi_slopes,
     lazy_attn_pack_segments,
     lazy_attn_validate_table,
     lazy_attn_decode_workspace_size,

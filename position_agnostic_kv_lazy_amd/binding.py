@@ -34,11 +34,13 @@ _lib = ctypes.CDLL(LIB_PATH)
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE_TOO_SMALL, LA_ERR_HIP = range(5)
 LA_BF16, LA_FP32 = 0, 1
 LA_POOL_POSITION_FREE, LA_POOL_DOC_LOCAL = 0, 1
+LA_ROPE_HALF, LA_ROPE_INTERLEAVED, LA_ALIBI = 0, 1, 2
 
 EXPORTED = (
     "lazy_attn_status_string",
     "lazy_attn_last_error",
     "lazy_attn_rope_table",
+    "lazy_attn_alibi_slopes",
     "lazy_attn_pack_segments",
     "lazy_attn_validate_table",
     "lazy_attn_decode_workspace_size",
@@ -61,7 +63,8 @@ class la_params(ctypes.Structure):
         ("split_blocks", ctypes.c_int32),
         ("target_workgroups", ctypes.c_int32),
         ("pool_mode", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 4),
+        ("pos_encoding", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
     ]
 
 
@@ -87,6 +90,8 @@ _lib.lazy_attn_last_error.restype = ctypes.c_char_p
 _lib.lazy_attn_last_error.argtypes = []
 _lib.lazy_attn_rope_table.restype = ctypes.c_int
 _lib.lazy_attn_rope_table.argtypes = [ctypes.c_double, ctypes.c_int32, ctypes.c_int32, _f32p]
+_lib.lazy_attn_alibi_slopes.restype = ctypes.c_int
+_lib.lazy_attn_alibi_slopes.argtypes = [ctypes.c_int32, _f32p]
 _lib.lazy_attn_pack_segments.restype = ctypes.c_int
 _lib.lazy_attn_pack_segments.argtypes = [_prm, ctypes.c_int32, _i64p, _i64p, _i64p, _u8p, _i64p,
                                          _i64p, _u64p, ctypes.c_int64, _i32p, _i32p]
@@ -111,7 +116,8 @@ def _check(status: int, func: str):
 
 
 def make_params(*, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, scale,
-                max_pos, split_blocks=0, target_workgroups=0, pool_mode=0) -> la_params:
+                max_pos, split_blocks=0, target_workgroups=0, pool_mode=0,
+                pos_encoding=0) -> la_params:
     p = la_params()
     p.num_q_heads = num_q_heads
     p.num_kv_heads = num_kv_heads
@@ -125,6 +131,8 @@ def make_params(*, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, 
     p.target_workgroups = target_workgroups
     p.pool_mode = {"position_free": LA_POOL_POSITION_FREE,
                    "doc_local": LA_POOL_DOC_LOCAL}.get(pool_mode, pool_mode)
+    p.pos_encoding = {"rope_half": LA_ROPE_HALF, "rope_interleaved": LA_ROPE_INTERLEAVED,
+                      "alibi": LA_ALIBI}.get(pos_encoding, pos_encoding)
     return p
 
 
@@ -158,6 +166,14 @@ def lazy_attn_rope_table(base: float, head_dim: int, rows: int) -> np.ndarray:
     out = np.empty((rows, head_dim), dtype=np.float32)
     _check(_lib.lazy_attn_rope_table(float(base), head_dim, rows,
                                      out.ctypes.data_as(_f32p)), "lazy_attn_rope_table")
+    return out
+
+
+def lazy_attn_alibi_slopes(num_heads: int) -> np.ndarray:
+    """Host float32 [num_heads] standard ALiBi slopes."""
+    out = np.empty(num_heads, dtype=np.float32)
+    _check(_lib.lazy_attn_alibi_slopes(num_heads, out.ctypes.data_as(_f32p)),
+           "lazy_attn_alibi_slopes")
     return out
 
 

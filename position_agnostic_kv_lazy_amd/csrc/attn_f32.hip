@@ -10,21 +10,27 @@
 // Document-local pools (keys stored as R_t k with t the index inside the
 // segment): decode rotates q by m - s per block (s = the segment start the word
 // carries) and uses the keys as stored; prefill rotates each key by s once
-// (for the causal blocks s is the request's first new position).
+// (for the causal blocks s is the request's first new position).  ALiBi: no
+// rotation; each score gets slope_h * (p - m).  Interleaved RoPE: lane i loads
+// q elements (2i, 2i+1); keys of such pools are stored (even, odd) dims.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace lazyattn {
 namespace {
 
-template <int D, bool DOC_LOCAL>
+// MODE: 0 RoPE over a position-free pool, 1 RoPE over a document-local pool,
+// 2 ALiBi (cs then holds the per-query-head slopes).
+template <int D, int MODE>
 __global__ __launch_bounds__(64) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k_pool,
     const float* __restrict__ v_pool, const uint64_t* __restrict__ words,
     const int32_t* __restrict__ req_blk_start, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ q_pos, const float* __restrict__ cs, int Hq, int Hkv, int BS,
-    float scale, float* __restrict__ out, float* __restrict__ lse) {
+    float scale, int interleaved, float* __restrict__ out, float* __restrict__ lse) {
   constexpr int HALF = D / 2;
+  constexpr bool DOC_LOCAL = MODE == 1;
+  constexpr bool ALIBI = MODE == 2;
   const int h = blockIdx.x;
   const int r = blockIdx.z;
   const int lane = threadIdx.x;
@@ -48,9 +54,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
   const float* qrow = q + (static_cast<size_t>(row) * Hq + h) * D;
   float q1 = 0.f, q2 = 0.f, x1 = 0.f, x2 = 0.f;
   if (active) {
-    x1 = qrow[i];
-    x2 = qrow[i + HALF];
-    if (!DOC_LOCAL || prefill) {
+    x1 = qrow[interleaved ? 2 * i : i];
+    x2 = qrow[interleaved ? 2 * i + 1 : i + HALF];
+    if (ALIBI) {
+      q1 = x1;
+      q2 = x2;
+    } else if (!DOC_LOCAL || prefill) {
       const float c = cs[static_cast<size_t>(qp) * D + i];
       const float s = cs[static_cast<size_t>(qp) * D + HALF + i];
       q1 = x1 * c - x2 * s;
@@ -79,7 +88,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
       float part = 0.f, v1 = 0.f, v2 = 0.f;
       if (active) {
         const float k1 = kb[t * D + i], k2 = kb[t * D + i + HALF];
-        if (DOC_LOCAL && !prefill) {
+        if (ALIBI || (DOC_LOCAL && !prefill)) {
           part = q1 * k1 + q2 * k2;
         } else {
           // key rotation: its position, or (doc-local) its segment's start
@@ -91,7 +100,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
         v1 = vb[i * BS + t];
         v2 = vb[(i + HALF) * BS + t];
       }
-      const float sc = wave_sum(part) * scale;
+      float sc = wave_sum(part) * scale;
+      if (ALIBI) sc += cs[h] * static_cast<float>(p - qp);
       const float mn = fmaxf(m, sc);
       const float corr = expf(m - mn);
       const float pe = expf(sc - mn);
@@ -115,20 +125,29 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 hipError_t launch_attn_f32(const AttnArgs& a, bool prefill, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, prefill ? a.max_q_per_req : 1, a.batch);
   const int32_t* cu = prefill ? a.cu_q : nullptr;
-#define LAZYATTN_F32(DIM, DOC)                                                               \
-  hipLaunchKernelGGL((attn_f32_kernel<DIM, DOC>), grid, dim3(64), 0, stream,                 \
+#define LAZYATTN_F32(DIM, MODE)                                                              \
+  hipLaunchKernelGGL((attn_f32_kernel<DIM, MODE>), grid, dim3(64), 0, stream,                \
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k_pool),    \
                      static_cast<const float*>(a.v_pool), a.words, a.req_blk_start, cu,      \
                      a.q_pos, a.cos_sin, a.num_q_heads, a.num_kv_heads, a.block_size,         \
-                     a.scale, static_cast<float*>(a.out), a.lse)
-  const bool doc = a.pool_mode == 1;
+                     a.scale, a.pos_encoding == 1 ? 1 : 0, static_cast<float*>(a.out), a.lse)
+#define LAZYATTN_F32_MODES(DIM)        \
+  if (mode == 0) {                     \
+    LAZYATTN_F32(DIM, 0);              \
+  } else if (mode == 1) {              \
+    LAZYATTN_F32(DIM, 1);              \
+  } else {                             \
+    LAZYATTN_F32(DIM, 2);              \
+  }
+  const int mode = a.pos_encoding == 2 ? 2 : (a.pool_mode == 1 ? 1 : 0);
   if (a.head_dim == 128) {
-    if (doc) LAZYATTN_F32(128, true); else LAZYATTN_F32(128, false);
+    LAZYATTN_F32_MODES(128)
   } else if (a.head_dim == 64) {
-    if (doc) LAZYATTN_F32(64, true); else LAZYATTN_F32(64, false);
+    LAZYATTN_F32_MODES(64)
   } else {
     return hipErrorInvalidValue;
   }
+#undef LAZYATTN_F32_MODES
 #undef LAZYATTN_F32
   return hipGetLastError();
 }

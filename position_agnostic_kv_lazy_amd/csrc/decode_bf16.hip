@@ -33,6 +33,12 @@
 // (R_{m-s} q)^T k_stored, so keys are used as loaded and q is rotated only when
 // s changes between consecutive blocks of a wave -- once per document run, the
 // decode design of the paper's §3.2 (Eq. 6).
+//
+// ALiBi (§3.5 "Score-space positional methods"): no rotation at all; the score
+// of key slot i gets slope_h * (pos0 + i - m), computed from the block word in
+// registers.  Interleaved RoPE pairs (2i, 2i+1) only change which q elements a
+// lane loads: such pools store keys in (even dims, odd dims) order, which makes
+// every pair (i, i + D/2) again.
 #include <climits>
 
 #include "device_common.hpp"
@@ -55,15 +61,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ i16x4 as_i16x4(uint2 u) { return __builtin_bit_cast(i16x4, u); }
 
-template <int G, bool DOC_LOCAL>
+// MODE: 0 RoPE over a position-free pool, 1 RoPE over a document-local pool,
+// 2 ALiBi (cs then holds the per-query-head slopes).
+template <int G, int MODE>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const uint64_t* __restrict__ words,
     const int32_t* __restrict__ req_blk_start, const int32_t* __restrict__ q_pos,
     const float* __restrict__ cs, int Hkv, int npairs, int groups, int group_blocks,
-    float qscale, float* __restrict__ part_o, float* __restrict__ part_ml,
+    float qscale, int interleaved, float* __restrict__ part_o, float* __restrict__ part_ml,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   static_assert(G >= 1 && G <= 16 && 64 % G == 0, "group size");
+  constexpr bool DOC_LOCAL = MODE == 1;
+  constexpr bool ALIBI = MODE == 2;
+  constexpr bool RAW_KEYS = MODE != 0;  // keys used as stored
   constexpr int LPH = 64 / G;  // rotation lanes per query head
   const int Hq = Hkv * G;
   const int pair = blockIdx.x % npairs;  // r * Hkv + g: same g -> same XCD
@@ -89,7 +100,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
   // Slot rotation of the key slot this lane owns: pairs j = 8*(4s+gq) + e.
   float cslot[2][8], sslot[2][8];
 #pragma unroll
-  for (int s = 0; s < 2 && !DOC_LOCAL; ++s) {
+  for (int s = 0; s < 2 && !RAW_KEYS; ++s) {
     const float* row = cs + static_cast<size_t>(n) * D + 8 * (4 * s + gq);
     const float4 c0 = *reinterpret_cast<const float4*>(row);
     const float4 c1 = *reinterpret_cast<const float4*>(row + 4);
@@ -106,13 +117,19 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
   const int pg = lane - hh * LPH;
   float qx1[G], qx2[G];
   {
-    const uint16_t* qrow = q + (static_cast<size_t>(r) * Hq + g * G + hh) * D + pg * G;
+    const uint16_t* qrow = q + (static_cast<size_t>(r) * Hq + g * G + hh) * D;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      qx1[u] = __uint_as_float(static_cast<uint32_t>(qrow[u]) << 16) * qscale;
-      qx2[u] = __uint_as_float(static_cast<uint32_t>(qrow[HALF + u]) << 16) * qscale;
+      const int i = pg * G + u;  // pair i: (i, i + D/2), or (2i, 2i + 1) interleaved
+      const int o1 = interleaved ? 2 * i : i;
+      const int o2 = interleaved ? 2 * i + 1 : i + HALF;
+      qx1[u] = __uint_as_float(static_cast<uint32_t>(qrow[o1]) << 16) * qscale;
+      qx2[u] = __uint_as_float(static_cast<uint32_t>(qrow[o2]) << 16) * qscale;
     }
   }
+  // ALiBi: this lane's column slope, in the log2 units of the scores.
+  float slope2 = 0.f;
+  if (ALIBI && n < G) slope2 = cs[g * G + n] * LOG2E;
 
   float mrun = -INFINITY, lrun = 0.f;
   int q_delta = INT_MIN;  // doc-local pools: segment start qbv was rotated for
@@ -135,8 +152,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
     for (int j = 0; j < 8; ++j) vr[j] = *reinterpret_cast<const uint2*>(vb + 16 * j * BS);
 
     // q_b = R_{m - pos0} q for this block (doc-local pools: R_{m - s}, only when
-    // the segment changes); R_{-x} has the sine negated.
-    const bool rotate_q = !DOC_LOCAL || w.pos0 != q_delta;
+    // the segment changes; ALiBi: q itself, once); R_{-x} has the sine negated.
+    const bool rotate_q = MODE == 0 ? true : (DOC_LOCAL ? w.pos0 != q_delta : q_delta == INT_MIN);
     if (rotate_q) {
       q_delta = w.pos0;
       int off = m - w.pos0;
@@ -146,17 +163,22 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
         sgn = -1.f;
       }
       {
-        const float* row = cs + static_cast<size_t>(off) * D + pg * G;
+        const float* row = ALIBI ? cs : cs + static_cast<size_t>(off) * D + pg * G;
         uint16_t* dst = &qb_lds[wave][hh][0];
 #pragma unroll
         for (int u = 0; u < G; u += 2) {
           float y1[2], y2[2];
 #pragma unroll
           for (int t = 0; t < 2 && u + t < G; ++t) {
-            const float c = row[u + t];
-            const float sn = sgn * row[HALF + u + t];
-            y1[t] = qx1[u + t] * c - qx2[u + t] * sn;
-            y2[t] = qx1[u + t] * sn + qx2[u + t] * c;
+            if (ALIBI) {
+              y1[t] = qx1[u + t];
+              y2[t] = qx2[u + t];
+            } else {
+              const float c = row[u + t];
+              const float sn = sgn * row[HALF + u + t];
+              y1[t] = qx1[u + t] * c - qx2[u + t] * sn;
+              y2[t] = qx1[u + t] * sn + qx2[u + t] * c;
+            }
           }
           if (G == 1) {
             dst[pg * G + u] = f32_to_bf16(y1[0]);
@@ -181,12 +203,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
 
     // K' = R_slot k (fp32), rounded to bf16 for the MFMA (doc-local: as stored).
     bf16x8 ka[4];
-    if (DOC_LOCAL) {
+    if (RAW_KEYS) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) ka[s] = as_bf16x8(kr[s]);
     }
 #pragma unroll
-    for (int s = 0; s < 2 && !DOC_LOCAL; ++s) {
+    for (int s = 0; s < 2 && !RAW_KEYS; ++s) {
       const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&kr[s]);
       const uint32_t* a2 = reinterpret_cast<const uint32_t*>(&kr[s + 2]);
       uint4 o1, o2;
@@ -216,6 +238,11 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qbv[s], sacc, 0, 0, 0);
 
     // sacc[i] = score(key slot 4*gq + i, head n), already scaled by scale*log2(e).
+    if (ALIBI) {
+      const float base = slope2 * static_cast<float>(w.pos0 + 4 * gq - m);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sacc[i] += __builtin_fmaf(slope2, static_cast<float>(i), base);
+    }
     if (w.n_valid < BS) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -328,7 +355,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   if (lse != nullptr && lane == 0) lse[rh] = L > 0.f ? (M + __log2f(L)) * LN2 : -INFINITY;
 }
 
-template <int G, bool DOC_LOCAL>
+template <int G, int MODE>
 hipError_t launch_g(const AttnArgs& a, const DecodeSplit& s, void* ws, hipStream_t stream) {
   const int npairs = a.batch * a.num_kv_heads;
   float* part_o = nullptr;
@@ -338,11 +365,12 @@ hipError_t launch_g(const AttnArgs& a, const DecodeSplit& s, void* ws, hipStream
     part_ml = part_o + static_cast<size_t>(a.batch) * a.num_q_heads * s.groups * D;
   }
   const float qscale = a.scale * LOG2E;
-  hipLaunchKernelGGL((decode_bf16_kernel<G, DOC_LOCAL>), dim3(npairs * s.groups), dim3(256), 0,
+  hipLaunchKernelGGL((decode_bf16_kernel<G, MODE>), dim3(npairs * s.groups), dim3(256), 0,
                      stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
                      static_cast<const uint16_t*>(a.v_pool), a.words, a.req_blk_start, a.q_pos,
-                     a.cos_sin, a.num_kv_heads, npairs, s.groups, s.group_blocks, qscale, part_o,
+                     a.cos_sin, a.num_kv_heads, npairs, s.groups, s.group_blocks, qscale,
+                     a.pos_encoding == 1 ? 1 : 0, part_o,
                      part_ml, static_cast<uint16_t*>(a.out), a.lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s.groups == 1) return e;
@@ -381,15 +409,21 @@ size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, const De
 
 hipError_t launch_decode_bf16(const AttnArgs& a, const DecodeSplit& s, void* workspace,
                               hipStream_t stream) {
-  const bool doc = a.pool_mode == 1;
+  const int mode = a.pos_encoding == 2 ? 2 : (a.pool_mode == 1 ? 1 : 0);
+#define LAZYATTN_DECODE_G(GG)                                      \
+  case GG:                                                         \
+    return mode == 0   ? launch_g<GG, 0>(a, s, workspace, stream)  \
+           : mode == 1 ? launch_g<GG, 1>(a, s, workspace, stream)  \
+                       : launch_g<GG, 2>(a, s, workspace, stream);
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return doc ? launch_g<1, true>(a, s, workspace, stream) : launch_g<1, false>(a, s, workspace, stream);
-    case 2: return doc ? launch_g<2, true>(a, s, workspace, stream) : launch_g<2, false>(a, s, workspace, stream);
-    case 4: return doc ? launch_g<4, true>(a, s, workspace, stream) : launch_g<4, false>(a, s, workspace, stream);
-    case 8: return doc ? launch_g<8, true>(a, s, workspace, stream) : launch_g<8, false>(a, s, workspace, stream);
-    case 16: return doc ? launch_g<16, true>(a, s, workspace, stream) : launch_g<16, false>(a, s, workspace, stream);
+    LAZYATTN_DECODE_G(1)
+    LAZYATTN_DECODE_G(2)
+    LAZYATTN_DECODE_G(4)
+    LAZYATTN_DECODE_G(8)
+    LAZYATTN_DECODE_G(16)
     default: return hipErrorInvalidValue;
   }
+#undef LAZYATTN_DECODE_G
 }
 
 }  // namespace lazyattn

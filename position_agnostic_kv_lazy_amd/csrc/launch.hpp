@@ -39,7 +39,8 @@ struct AttnArgs {
   int max_q_per_req;   // prefill
   int max_blocks_per_req;
   float scale;
-  int pool_mode;  // la_pool_mode
+  int pool_mode;     // la_pool_mode
+  int pos_encoding;  // la_pos_encoding; ALiBi: cos_sin holds the per-head slopes
 };
 
 // fp32 test-mode kernels (decode and prefill share one kernel).
@@ -53,9 +54,11 @@ hipError_t launch_decode_bf16(const AttnArgs& a, const DecodeSplit& s, void* wor
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
 
 // Cache write of n_tokens keys/values (keys optionally pre-rotated).
+// interleaved: keys arrive with RoPE pairs (2i, 2i+1) and are stored in
+// (even dims, odd dims) order.
 hipError_t launch_store_kv(const void* k, const void* v, int64_t n_tokens, const int64_t* slots,
                            const int32_t* rope_pos, const float* cos_sin, int num_kv_heads,
-                           int head_dim, int block_size, bool bf16, void* k_pool, void* v_pool,
-                           hipStream_t stream);
+                           int head_dim, int block_size, bool bf16, bool interleaved,
+                           void* k_pool, void* v_pool, hipStream_t stream);
 
 }  // namespace lazyattn

@@ -60,10 +60,15 @@ la_status check_params(const la_params* p) {
   if (!std::isfinite(p->scale)) return fail(LA_ERR_INVALID_ARG, "scale is not finite");
   if (p->split_blocks < 0 || p->target_workgroups < 0)
     return fail(LA_ERR_INVALID_ARG, "split_blocks / target_workgroups must be >= 0");
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 3; ++i)
     if (p->reserved[i] != 0) return fail(LA_ERR_INVALID_ARG, "reserved fields must be zero");
   if (p->pool_mode != LA_POOL_POSITION_FREE && p->pool_mode != LA_POOL_DOC_LOCAL)
     return fail(LA_ERR_INVALID_ARG, "unknown pool_mode %d", p->pool_mode);
+  if (p->pos_encoding != LA_ROPE_HALF && p->pos_encoding != LA_ROPE_INTERLEAVED &&
+      p->pos_encoding != LA_ALIBI)
+    return fail(LA_ERR_INVALID_ARG, "unknown pos_encoding %d", p->pos_encoding);
+  if (p->pos_encoding == LA_ALIBI && p->pool_mode != LA_POOL_POSITION_FREE)
+    return fail(LA_ERR_INVALID_ARG, "ALiBi reads position-free pools only");
   if (p->dtype == LA_FP32) {
     if (p->head_dim != 64 && p->head_dim != 128)
       return fail(LA_ERR_UNSUPPORTED, "fp32 mode supports head_dim 64 or 128, got %d",
@@ -117,6 +122,7 @@ lazyattn::AttnArgs make_args(const la_params* p, const void* q, const void* k_po
   a.max_blocks_per_req = max_blocks;
   a.scale = p->scale;
   a.pool_mode = p->pool_mode;
+  a.pos_encoding = p->pos_encoding;
   return a;
 }
 
@@ -182,6 +188,23 @@ LA_API la_status lazy_attn_rope_table(double base, int32_t head_dim, int32_t row
     return ok();
   } catch (...) {
     return fail(LA_ERR_INVALID_ARG, "unexpected exception in lazy_attn_rope_table");
+  }
+}
+
+LA_API la_status lazy_attn_alibi_slopes(int32_t num_heads, float* out) {
+  try {
+    if (out == nullptr) return fail(LA_ERR_INVALID_ARG, "out is NULL");
+    if (num_heads < 1 || num_heads > 65536)
+      return fail(LA_ERR_INVALID_ARG, "num_heads must be in [1, 65536], got %d", num_heads);
+    int p2 = 1;
+    while (p2 * 2 <= num_heads) p2 *= 2;
+    // slope k (1-based) of the n-head sequence is 2^(-8k/n)
+    for (int k = 0; k < p2; ++k) out[k] = static_cast<float>(std::exp2(-8.0 * (k + 1) / p2));
+    for (int k = 0; k < num_heads - p2; ++k)
+      out[p2 + k] = static_cast<float>(std::exp2(-8.0 * (2 * k + 1) / (2.0 * p2)));
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_INVALID_ARG, "unexpected exception in lazy_attn_alibi_slopes");
   }
 }
 
@@ -353,7 +376,8 @@ LA_API la_status lazy_attn_store_kv(const la_params* p, const void* k, const voi
         return fail(LA_ERR_INVALID_ARG, "k, v, k_pool and v_pool must be 16-byte aligned");
     const hipError_t e = lazyattn::launch_store_kv(
         k, v, n_tokens, slots, rope_pos, cos_sin, p->num_kv_heads, p->head_dim, p->block_size,
-        p->dtype == LA_BF16, k_pool, v_pool, static_cast<hipStream_t>(stream));
+        p->dtype == LA_BF16, p->pos_encoding == LA_ROPE_INTERLEAVED, k_pool, v_pool,
+        static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "lazy_attn_store_kv launch");
     return ok();
   } catch (...) {

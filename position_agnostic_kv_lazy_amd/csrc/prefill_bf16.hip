@@ -31,6 +31,11 @@
 // word carries (for causal blocks, whose words keep slot 0's position for the
 // mask, s is the request's first new position), so one table row serves a
 // whole document -- the single relative rotation of §3.2 "Prefilling".
+//
+// ALiBi (§3.5): neither q nor keys are rotated; each score gets
+// slope_h * (p - m) in fp32 after the S product.  Interleaved RoPE pairs
+// (2i, 2i+1) only change how q is loaded (keys of such pools are stored in
+// (even dims, odd dims) order, so every pair is (i, i + D/2) again).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -72,14 +77,18 @@ struct Staged {
   uint4 v[2];        // two 16-byte V^T chunks (unused slots zeroed)
 };
 
-template <int G, bool DOC_LOCAL>
+// MODE: 0 RoPE over a position-free pool, 1 RoPE over a document-local pool,
+// 2 ALiBi (cs then holds the per-query-head slopes).
+template <int G, int MODE>
 __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const uint64_t* __restrict__ words,
     const int32_t* __restrict__ req_blk_start, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ q_pos0, const float* __restrict__ cs, int Hkv, int npairs,
-    float qscale, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    float qscale, int interleaved, uint16_t* __restrict__ out, float* __restrict__ lse) {
   static_assert(ROWS % G == 0, "group size must divide 256");
+  constexpr bool DOC_LOCAL = MODE == 1;
+  constexpr bool ALIBI = MODE == 2;
   constexpr int TQ = ROWS / G;  // new tokens per workgroup
   const int Hq = Hkv * G;
   const int pair = blockIdx.x % npairs;  // r * Hkv + g: same g -> same XCD
@@ -107,20 +116,45 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
   const bool row_valid = jt < nq;
   const int qpos = p0 + (row_valid ? jt : 0);
   bf16x8 qb[8];  // B operand of K'Q^T, k-step s covers dims 16s .. 16s+15
+  float slope2 = 0.f;  // ALiBi slope of this lane's head, log2 units
   {
-    uint4 raw[8];
+    uint4 raw[8];  // raw[s], raw[s + 4]: x1 and x2 of pairs 16s + 8h2 .. +7 (s < 4)
     const uint16_t* qrow =
         q + (static_cast<size_t>(q_begin + (row_valid ? jt : 0)) * Hq + head) * D;
+    if (interleaved) {
+      // pairs j0 .. j0+7 are dims 2j0 .. 2j0+15: split even (x1) and odd (x2) halves
 #pragma unroll
-    for (int s = 0; s < 8; ++s) raw[s] = *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * h2);
-    const float* crow = cs + static_cast<size_t>(qpos) * D;
+      for (int s = 0; s < 4; ++s) {
+        const int j0 = 16 * s + 8 * h2;
+        const uint4 a = *reinterpret_cast<const uint4*>(qrow + 2 * j0);
+        const uint4 b = *reinterpret_cast<const uint4*>(qrow + 2 * j0 + 8);
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t ev[4], od[4];
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+          ev[k2] = (w[2 * k2] & 0xFFFFu) | (w[2 * k2 + 1] << 16);
+          od[k2] = (w[2 * k2] >> 16) | (w[2 * k2 + 1] & 0xFFFF0000u);
+        }
+        raw[s] = uint4{ev[0], ev[1], ev[2], ev[3]};
+        raw[s + 4] = uint4{od[0], od[1], od[2], od[3]};
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) raw[s] = *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * h2);
+    }
+    const float* crow = ALIBI ? cs : cs + static_cast<size_t>(qpos) * D;
+    if (ALIBI) slope2 = cs[head] * LOG2E;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int j0 = 16 * s + 8 * h2;  // pairs j0 .. j0+7, partners at +64
-      const float4 c0 = *reinterpret_cast<const float4*>(crow + j0);
-      const float4 c1 = *reinterpret_cast<const float4*>(crow + j0 + 4);
-      const float4 s0 = *reinterpret_cast<const float4*>(crow + HALF + j0);
-      const float4 s1 = *reinterpret_cast<const float4*>(crow + HALF + j0 + 4);
+      float4 c0 = float4{1.f, 1.f, 1.f, 1.f}, c1 = c0;
+      float4 s0 = float4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+      if (!ALIBI) {
+        c0 = *reinterpret_cast<const float4*>(crow + j0);
+        c1 = *reinterpret_cast<const float4*>(crow + j0 + 4);
+        s0 = *reinterpret_cast<const float4*>(crow + HALF + j0);
+        s1 = *reinterpret_cast<const float4*>(crow + HALF + j0 + 4);
+      }
       const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
       const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
       const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&raw[s]);
@@ -182,7 +216,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     if (tb + kblk < rb1) {
       const BlockWord w = unpack_word(words[tb + kblk]);
       const uint16_t* kb = k_pool + (static_cast<size_t>(w.block_id) * Hkv + g) * (BS * D);
-      if (DOC_LOCAL) {
+      if (ALIBI) {
+        row = cs;  // no table: keys are not rotated
+      } else if (DOC_LOCAL) {
         row = cs + static_cast<size_t>(w.causal ? p0 : w.pos0) * D + 8 * cp;
       } else {
         // unused slots keep K = 0 and read the table row of the block's last key
@@ -195,10 +231,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
         st.k2 = *reinterpret_cast<const uint4*>(kb + off + HALF);
       }
     }
-    st.c0 = *reinterpret_cast<const float4*>(row);
-    st.c1 = *reinterpret_cast<const float4*>(row + 4);
-    st.s0 = *reinterpret_cast<const float4*>(row + HALF);
-    st.s1 = *reinterpret_cast<const float4*>(row + HALF + 4);
+    if (!ALIBI) {
+      st.c0 = *reinterpret_cast<const float4*>(row);
+      st.c1 = *reinterpret_cast<const float4*>(row + 4);
+      st.s0 = *reinterpret_cast<const float4*>(row + HALF);
+      st.s1 = *reinterpret_cast<const float4*>(row + HALF + 4);
+    } else {
+      st.c0 = st.c1 = st.s0 = st.s1 = float4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int vb = 2 * u + (wave_u >> 2);
@@ -226,11 +266,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     const float ss[8] = {st.s0.x, st.s0.y, st.s0.z, st.s0.w, st.s1.x, st.s1.y, st.s1.z, st.s1.w};
     const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&st.k1);
     const uint32_t* a2 = reinterpret_cast<const uint32_t*>(&st.k2);
-    uint4 o1, o2;
+    uint4 o1 = st.k1, o2 = st.k2;  // ALiBi: keys go to LDS as stored
     uint32_t* p1 = reinterpret_cast<uint32_t*>(&o1);
     uint32_t* p2 = reinterpret_cast<uint32_t*>(&o2);
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
+    for (int e2 = 0; e2 < 4 && !ALIBI; ++e2) {
       float y1[2], y2[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -314,6 +354,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
         sacc[tk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qb[s], sacc[tk], 0, 0, 0);
       }
     // sacc[tk][rr] = score(key 32tk + 8(rr/4) + 4h2 + rr%4, this lane's row) - mref
+    if (ALIBI) {
+      // + slope * (p - m); the key of sacc[tk][rr] is slot 8((rr/4)%2) + 4h2 + rr%4 of
+      // block 2tk + rr/8
+      float base[BPT];
+#pragma unroll
+      for (int b = 0; b < BPT; ++b) base[b] = slope2 * static_cast<float>(t_pos0[b] + 4 * h2 - qpos);
+#pragma unroll
+      for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+          sacc[tk][rr] += __builtin_fmaf(slope2, static_cast<float>(8 * ((rr >> 2) & 1) + (rr & 3)),
+                                         base[2 * tk + (rr >> 3)]);
+    }
     if (!tile_simple) {
       // Visible slots of block bb are [0, lim[bb]).  Routing the limits through
       // an empty asm inside this (wave-uniform) branch keeps the compiler from
@@ -345,14 +398,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     float delta = 0.f;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
       // New reference for the rows that need one; the others keep theirs.
+      // A row's first reference may lie far below 0 (very negative scores):
+      // nothing is accumulated yet, so it takes no rescale (exp2(-delta)
+      // would overflow).
+      float alpha = 1.f;
       if (raise) {
         const float mnew = __uint_as_float(static_cast<uint32_t>(f32_to_bf16(mref + tmax)) << 16);
         delta = mnew - mref;
+        if (mset) alpha = __builtin_amdgcn_exp2f(-delta);
         mref = mnew;
         mset = true;
         negm_b = as_bf16x8(uint4{h2 == 0 ? static_cast<uint32_t>(f32_to_bf16(-mref)) : 0u, 0u, 0u, 0u});
       }
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
       lrun *= alpha;
 #pragma unroll
       for (int t = 0; t < 4; ++t) oacc[t] *= alpha;
@@ -412,32 +469,38 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
         lrun > 0.f ? (mref + __log2f(lrun)) * LN2 : -INFINITY;
 }
 
-template <int G, bool DOC_LOCAL>
+template <int G, int MODE>
 hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
   constexpr int TQ = ROWS / G;
   const int npairs = a.batch * a.num_kv_heads;
   const int qtiles = (a.max_q_per_req + TQ - 1) / TQ;
-  hipLaunchKernelGGL((prefill_bf16_kernel<G, DOC_LOCAL>), dim3(npairs * qtiles), dim3(NTHREADS), 0,
+  hipLaunchKernelGGL((prefill_bf16_kernel<G, MODE>), dim3(npairs * qtiles), dim3(NTHREADS), 0,
                      stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
                      static_cast<const uint16_t*>(a.v_pool), a.words, a.req_blk_start, a.cu_q,
                      a.q_pos, a.cos_sin, a.num_kv_heads, npairs, a.scale * LOG2E,
-                     static_cast<uint16_t*>(a.out), a.lse);
+                     a.pos_encoding == 1 ? 1 : 0, static_cast<uint16_t*>(a.out), a.lse);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
-  const bool doc = a.pool_mode == 1;
+  const int mode = a.pos_encoding == 2 ? 2 : (a.pool_mode == 1 ? 1 : 0);
+#define LAZYATTN_PREFILL_G(GG)                                                   \
+  case GG:                                                                       \
+    return mode == 0   ? launch_g<GG, 0>(a, stream)                              \
+           : mode == 1 ? launch_g<GG, 1>(a, stream)                              \
+                       : launch_g<GG, 2>(a, stream);
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return doc ? launch_g<1, true>(a, stream) : launch_g<1, false>(a, stream);
-    case 2: return doc ? launch_g<2, true>(a, stream) : launch_g<2, false>(a, stream);
-    case 4: return doc ? launch_g<4, true>(a, stream) : launch_g<4, false>(a, stream);
-    case 8: return doc ? launch_g<8, true>(a, stream) : launch_g<8, false>(a, stream);
-    case 16: return doc ? launch_g<16, true>(a, stream) : launch_g<16, false>(a, stream);
+    LAZYATTN_PREFILL_G(1)
+    LAZYATTN_PREFILL_G(2)
+    LAZYATTN_PREFILL_G(4)
+    LAZYATTN_PREFILL_G(8)
+    LAZYATTN_PREFILL_G(16)
     default: return hipErrorInvalidValue;
   }
+#undef LAZYATTN_PREFILL_G
 }
 
 }  // namespace lazyattn

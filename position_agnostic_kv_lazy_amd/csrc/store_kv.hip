@@ -14,6 +14,10 @@
 // its 16 tokens fill one whole block in slot order (the common case: a
 // document written front to back), written as 16-byte rows of the dim-major
 // tile; any other slot pattern falls back to one element per store.
+//
+// Interleaved RoPE keys (pairs (2i, 2i+1)) are rotated on those pairs and
+// stored in (even dims, odd dims) order, so pair i lands on (i, i + D/2) and
+// the attention kernels treat both pairings alike.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -48,8 +52,8 @@ template <bool BF16, int D>
 __global__ __launch_bounds__(NT) void store_kv_kernel(
     const typename Elem<BF16>::T* __restrict__ k, const typename Elem<BF16>::T* __restrict__ v,
     int64_t n_tokens, const int64_t* __restrict__ slots, const int32_t* __restrict__ rope_pos,
-    const float* __restrict__ cs, int Hkv, int BS, typename Elem<BF16>::T* __restrict__ k_pool,
-    typename Elem<BF16>::T* __restrict__ v_pool) {
+    const float* __restrict__ cs, int Hkv, int BS, int interleaved,
+    typename Elem<BF16>::T* __restrict__ k_pool, typename Elem<BF16>::T* __restrict__ v_pool) {
   using E = Elem<BF16>;
   using T = typename E::T;
   constexpr int HALF = D / 2;
@@ -69,8 +73,22 @@ __global__ __launch_bounds__(NT) void store_kv_kernel(
   if (live) {
     slot = slots[t];
     const size_t src = (static_cast<size_t>(t) * Hkv + h) * D + P * l;
-    const V a = *reinterpret_cast<const V*>(k + src);
-    const V b = *reinterpret_cast<const V*>(k + src + HALF);
+    V a, b;  // x1, x2 of pairs P*l .. P*l + P-1
+    if (interleaved) {
+      const size_t row = (static_cast<size_t>(t) * Hkv + h) * D + 2 * P * l;
+      const V lo = *reinterpret_cast<const V*>(k + row);
+      const V hi = *reinterpret_cast<const V*>(k + row + P);
+#pragma unroll
+      for (int u = 0; u < P / 2; ++u) {
+        a.e[u] = lo.e[2 * u];
+        b.e[u] = lo.e[2 * u + 1];
+        a.e[P / 2 + u] = hi.e[2 * u];
+        b.e[P / 2 + u] = hi.e[2 * u + 1];
+      }
+    } else {
+      a = *reinterpret_cast<const V*>(k + src);
+      b = *reinterpret_cast<const V*>(k + src + HALF);
+    }
     V ya = a, yb = b;
     if (rope_pos != nullptr) {
       const float* row = cs + static_cast<size_t>(rope_pos[t]) * D + P * l;
@@ -130,15 +148,15 @@ __global__ __launch_bounds__(NT) void store_kv_kernel(
 
 hipError_t launch_store_kv(const void* k, const void* v, int64_t n_tokens, const int64_t* slots,
                            const int32_t* rope_pos, const float* cos_sin, int num_kv_heads,
-                           int head_dim, int block_size, bool bf16, void* k_pool, void* v_pool,
-                           hipStream_t stream) {
+                           int head_dim, int block_size, bool bf16, bool interleaved,
+                           void* k_pool, void* v_pool, hipStream_t stream) {
   if (n_tokens == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((n_tokens + CHUNK - 1) / CHUNK), num_kv_heads);
 #define LAZYATTN_STORE(B, DIM)                                                                 \
   hipLaunchKernelGGL((store_kv_kernel<B, DIM>), grid, dim3(NT), 0, stream,                     \
                      static_cast<const typename Elem<B>::T*>(k),                               \
                      static_cast<const typename Elem<B>::T*>(v), n_tokens, slots, rope_pos,     \
-                     cos_sin, num_kv_heads, block_size,                                         \
+                     cos_sin, num_kv_heads, block_size, interleaved ? 1 : 0,                    \
                      static_cast<typename Elem<B>::T*>(k_pool),                                 \
                      static_cast<typename Elem<B>::T*>(v_pool))
   if (bf16 && head_dim == 128) {

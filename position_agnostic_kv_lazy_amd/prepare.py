@@ -86,23 +86,28 @@ class DeviceBatch:
 
 
 def params_for(w, num_blocks: int, max_pos: Optional[int] = None, split_blocks: int = 0,
-               target_workgroups: int = 0, pool_mode="position_free") -> B.la_params:
+               target_workgroups: int = 0, pool_mode="position_free",
+               pos_encoding="rope_half") -> B.la_params:
     """la_params describing batch w over a pool of num_blocks blocks."""
     rows = int(max_pos) if max_pos is not None else int(w.table_rows())
     return B.make_params(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                          head_dim=w.head_dim, block_size=w.block_size, num_blocks=int(num_blocks),
                          dtype=w.dtype, scale=w.scale, max_pos=rows, split_blocks=split_blocks,
-                         target_workgroups=target_workgroups, pool_mode=pool_mode)
+                         target_workgroups=target_workgroups, pool_mode=pool_mode,
+                         pos_encoding=pos_encoding)
 
 
 def store_pool(w, k_tok: np.ndarray, v_tok: np.ndarray, slots: np.ndarray,
                rope_pos: Optional[np.ndarray], device="cuda", num_blocks: Optional[int] = None,
-               max_pos: Optional[int] = None, fill: float = 0.0, stream=None):
+               max_pos: Optional[int] = None, fill: float = 0.0, stream=None,
+               pos_encoding="rope_half"):
     """Build a device pool pair by writing tokens with lazy_attn_store_kv.
 
     k_tok / v_tok: host [n, Hkv, D] in the pool encoding; slots: flat slot ids;
     rope_pos: per-token rotation position or None (keys stored as given).
-    Unlisted slots hold `fill`.  Returns (k_dev, v_dev) in the device layouts.
+    pos_encoding="rope_interleaved" rotates pairs (2i, 2i+1) and stores keys in
+    (even dims, odd dims) order.  Unlisted slots hold `fill`.  Returns
+    (k_dev, v_dev) in the device layouts.
     """
     nb = int(num_blocks) if num_blocks is not None else int(w.num_blocks)
     rows = int(max_pos) if max_pos is not None else int(w.table_rows())
@@ -116,7 +121,7 @@ def store_pool(w, k_tok: np.ndarray, v_tok: np.ndarray, slots: np.ndarray,
         raise ValueError("rope position outside the cos/sin table")
     if k_tok.shape != (len(slots), w.num_kv_heads, w.head_dim) or v_tok.shape != k_tok.shape:
         raise ValueError("k/v token arrays must be [n, Hkv, D]")
-    params = params_for(w, nb, rows)
+    params = params_for(w, nb, rows, pos_encoding=pos_encoding)
     bf16 = k_tok.dtype == np.uint16
     dt = torch.int16 if bf16 else torch.float32
     Hkv, BS, D = w.num_kv_heads, w.block_size, w.head_dim
@@ -141,12 +146,21 @@ def store_pool(w, k_tok: np.ndarray, v_tok: np.ndarray, slots: np.ndarray,
 
 def prepare(w, k_dev: torch.Tensor, v_dev: torch.Tensor, device="cuda", split_blocks: int = 0,
             target_workgroups: int = 0, max_pos: Optional[int] = None,
-            pool_mode="position_free") -> DeviceBatch:
-    """Pack and upload everything lazy_attn_decode/prefill need for batch w."""
+            pool_mode="position_free", pos_encoding="rope_half",
+            table: Optional[np.ndarray] = None) -> DeviceBatch:
+    """Pack and upload everything lazy_attn_decode/prefill need for batch w.
+
+    table overrides the position table handed to the kernels: by default the
+    RoPE cos/sin rows (lazy_attn_rope_table) or, for ALiBi, the standard
+    slopes (lazy_attn_alibi_slopes).
+    """
     rows = int(max_pos) if max_pos is not None else int(w.table_rows())
-    params = params_for(w, int(k_dev.shape[0]), rows, split_blocks, target_workgroups, pool_mode)
+    params = params_for(w, int(k_dev.shape[0]), rows, split_blocks, target_workgroups, pool_mode,
+                        pos_encoding)
     words, rbs, maxb = B.lazy_attn_pack_segments(params, w.requests)
-    table = B.lazy_attn_rope_table(w.rope_base, w.head_dim, rows)
+    if table is None:
+        table = (B.lazy_attn_alibi_slopes(w.num_q_heads) if pos_encoding == "alibi"
+                 else B.lazy_attn_rope_table(w.rope_base, w.head_dim, rows))
     q = _to_device_bits(w.q, device)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=device)
@@ -166,5 +180,6 @@ def prepare(w, k_dev: torch.Tensor, v_dev: torch.Tensor, device="cuda", split_bl
         kind=w.kind, params=params, q=q, k_pool=k_dev, v_pool=v_dev,
         words=torch.from_numpy(words.view(np.int64)).to(device),
         req_blk_start=torch.from_numpy(rbs).to(device), q_pos=q_pos, cu_q=cu_q,
-        cos_sin=torch.from_numpy(table).to(device), out=out, lse=lse, workspace=ws,
+        cos_sin=torch.from_numpy(np.ascontiguousarray(table, np.float32)).to(device), out=out,
+        lse=lse, workspace=ws,
         batch=w.batch, max_blocks=maxb, max_q=max_q, host_words=words, host_rbs=rbs)

@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -39,7 +39,7 @@ def test_status_strings():
 
 
 def test_params_struct_layout():
-    # int32 x4, int64, int32, float, int32 x4, int32[4] -> 64 bytes, int64 at offset 16
+    # int32 x4, int64, int32, float, int32 x5, int32[3] -> 64 bytes, int64 at offset 16
     assert ctypes.sizeof(B.la_params) == 64
     assert B.la_params.num_blocks.offset == 16
 
@@ -255,3 +255,22 @@ def test_one_hip_runtime_whatever_the_import_order():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
                          check=True).stdout.strip()
     assert out == "1", out
+
+
+def test_alibi_slopes_match_oracle():
+    from oracle import alibi_slopes
+    for n in (1, 8, 12, 32, 71):
+        got = la.lazy_attn_alibi_slopes(n)
+        np.testing.assert_allclose(got, alibi_slopes(n), rtol=2e-7, atol=0)
+    with pytest.raises(la.LazyAttnError, match="num_heads"):
+        la.lazy_attn_alibi_slopes(0)
+
+
+def test_pos_encoding_checks():
+    with pytest.raises(la.LazyAttnError, match="pos_encoding"):
+        la.lazy_attn_decode_workspace_size(_params(pos_encoding=3), 4, 10)
+    with pytest.raises(la.LazyAttnError, match="ALiBi reads position-free"):
+        la.lazy_attn_decode_workspace_size(_params(pos_encoding="alibi", pool_mode="doc_local"),
+                                           4, 10)
+    for enc in ("rope_half", "rope_interleaved", "alibi"):
+        la.lazy_attn_decode_workspace_size(_params(pos_encoding=enc), 4, 10)

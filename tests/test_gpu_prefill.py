@@ -108,3 +108,28 @@ def test_config5_prefill_sampled():
     rng = np.random.default_rng(35)
     rows = {r: _sample_rows(m.prefill.q_len(r), rng, extra=(511, 512, 1023)) for r in range(4)}
     _check_rows(m.prefill, out, lse, rows, "cfg5-pre")
+
+
+def test_first_tile_far_below_zero():
+    """A row whose first key tile scores far below 0 (< -128 in log2 units).
+
+    The kernel's first softmax reference for that row then lies far below the
+    initial 0; the accumulators must not be rescaled by exp2(-delta), which
+    overflows.  Identity cos/sin table, so the oracle is plain attention.
+    """
+    from workloads import f32_to_bf16_bits
+    w = _tiny(requests=[[("doc", 0), ("doc", 1), ("new", 40)]], doc_lens=(64, 37))
+    blocks = np.asarray(w.requests[0][0].blocks)
+    spike = np.zeros(w.head_dim, np.float32)
+    spike[0] = 40.0
+    w.k_pool[blocks] = f32_to_bf16_bits(spike)  # every key of doc 0 = 40 e_0
+    qf = w.values_f32(w.q).copy()
+    qf[..., 0] = -40.0  # q . k = -1600 on doc 0: about -204 in log2 units after scaling
+    w.q = f32_to_bf16_bits(qf)
+    ident = np.zeros((w.table_rows(), w.head_dim), np.float32)
+    ident[:, : w.head_dim // 2] = 1.0
+    out, lse, _ = Device(w).run(w, table=ident)
+    ref = run_prefill(w, rotate=False)
+    a, b = int(w.cu_q[0]), int(w.cu_q[1])
+    assert_parity(out[a:b], ref[0][0], "bf16", "far-negative first tile")
+    assert_lse(lse[a:b], ref[0][1], "bf16", "far-negative first tile")
