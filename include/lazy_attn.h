@@ -176,6 +176,46 @@ LA_API const char* lazy_attn_last_error(void);
 LA_API la_status lazy_attn_rope_table(double base, int32_t head_dim, int32_t rows, float* out);
 
 /*
+ * Scaled RoPE variants (§3.5: scaled / NTK / YaRN keep the score
+ * q^T R_{n-m} k; only the cos/sin table changes).  The published variants:
+ *  LA_SCALING_LINEAR  position interpolation: theta_i / factor
+ *  LA_SCALING_NTK     NTK-aware: base * factor^(D / (D - 2))
+ *  LA_SCALING_YARN    per pair, theta_i for pairs that turn more than
+ *                     beta_fast times over original_max_pos, theta_i / factor
+ *                     for pairs that turn less than beta_slow times, a linear
+ *                     ramp over the pair index in between; cos and sin are
+ *                     multiplied by attn_factor (0 = 0.1 ln(factor) + 1)
+ *  LA_SCALING_LLAMA3  wavelength 2 pi / theta_i below original_max_pos /
+ *                     high_freq_factor kept, above original_max_pos /
+ *                     low_freq_factor divided by factor, smooth in between
+ */
+typedef enum la_rope_scaling_type {
+  LA_SCALING_NONE = 0,
+  LA_SCALING_LINEAR = 1,
+  LA_SCALING_NTK = 2,
+  LA_SCALING_YARN = 3,
+  LA_SCALING_LLAMA3 = 4
+} la_rope_scaling_type;
+
+typedef struct la_rope_scaling {
+  int32_t type;              /* la_rope_scaling_type */
+  int32_t original_max_pos;  /* YARN, LLAMA3: pre-training context length */
+  double factor;             /* > 0 (1 = no scaling) */
+  double low_freq_factor;    /* LLAMA3 */
+  double high_freq_factor;   /* LLAMA3, > low_freq_factor */
+  double beta_fast;          /* YARN, e.g. 32 */
+  double beta_slow;          /* YARN, e.g. 1 */
+  double attn_factor;        /* YARN, 0 = default */
+} la_rope_scaling;
+
+/*
+ * lazy_attn_rope_table with a scaled variant (NULL or LA_SCALING_NONE: the
+ * plain table).  Same layout, float64 arithmetic, one rounding to float32.
+ */
+LA_API la_status lazy_attn_rope_table_scaled(double base, int32_t head_dim, int32_t rows,
+                                             const la_rope_scaling* scaling, float* out);
+
+/*
  * Standard ALiBi slopes for num_heads heads (host): 2^(-8/n), 2^(-16/n), ...
  * for n a power of two; otherwise the nearest lower power of two's sequence
  * followed by every other slope of the next power of two's sequence.

@@ -18,6 +18,7 @@ from .lazy_oracle import (  # noqa: F401
     rope_theta,
     rope_rotate,
     alibi_slopes,
+    rope_theta_scaled,
     gather_request,
     attention_decode,
     attention_prefill,

@@ -37,6 +37,7 @@ __all__ = [
     "rope_theta",
     "rope_rotate",
     "alibi_slopes",
+    "rope_theta_scaled",
     "gather_request",
     "attention_decode",
     "attention_prefill",
@@ -65,7 +66,7 @@ def rope_theta(head_dim: int, base: float) -> np.ndarray:
     return np.power(float(base), -2.0 * i / float(head_dim))
 
 
-def rope_rotate(x, pos, theta, pairing: str = "half") -> np.ndarray:
+def rope_rotate(x, pos, theta, pairing: str = "half", amp: float = 1.0) -> np.ndarray:
     """Rotate x[..., D] to position(s) pos (broadcast over leading axes).
 
     pairing="half": pair (i, i+D/2) is rotated by angle pos*theta_i:
@@ -77,12 +78,13 @@ def rope_rotate(x, pos, theta, pairing: str = "half") -> np.ndarray:
     Pins: equals multiplication of x_i + j x_{i+D/2} (interleaved:
     x_{2i} + j x_{2i+1}) by exp(j pos theta_i) (RoPE's complex form, computed
     with numpy complex arithmetic); Fact 3.2 (R_m q).(R_n k) = q.R_{n-m} k;
-    norm preservation; rot(x, 0) = x.
+    norm preservation; rot(x, 0) = x.  amp scales cos and sin alike (the
+    attention factor of YaRN tables).
     """
     x = np.asarray(x, dtype=np.float64)
     pos = np.asarray(pos, dtype=np.float64)
     ang = pos[..., None] * np.asarray(theta, dtype=np.float64)
-    c, s = np.cos(ang), np.sin(ang)
+    c, s = amp * np.cos(ang), amp * np.sin(ang)
     if pairing == "interleaved":
         x1, x2 = x[..., 0::2], x[..., 1::2]
         y = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (x.shape[-1],)))
@@ -94,6 +96,67 @@ def rope_rotate(x, pos, theta, pairing: str = "half") -> np.ndarray:
     half = x.shape[-1] // 2
     x1, x2 = x[..., :half], x[..., half:]
     return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def rope_theta_scaled(head_dim: int, base: float, scaling=None):
+    """Frequencies and amplitude of the scaled RoPE variants of §3.5.
+
+    The paper only says that scaled / NTK / YaRN variants keep the score
+    q^T R_{n-m} k with variant-specific metadata; the variants themselves are
+    the published ones, restated here (float64):
+      linear  (position interpolation): theta_i / s;
+      ntk     (NTK-aware): base' = base * s^(D / (D - 2));
+      yarn:   per pair, wavelength-dependent blend of theta_i (fast pairs) and
+              theta_i / s (slow pairs) over a linear ramp between the pair
+              indices where the rotation count over the original context is
+              beta_fast and beta_slow; cos and sin scaled by the attention
+              factor (default 0.1 ln s + 1);
+      llama3: wavelength 2 pi / theta_i below L/high_freq_factor kept, above
+              L/low_freq_factor divided by s, smooth blend in between.
+    scaling: None or a dict with "type" and the parameters above
+    (factor, original_max_pos, beta_fast, beta_slow, attn_factor,
+    low_freq_factor, high_freq_factor).  Returns (theta [D/2], amplitude).
+
+    Pins (tests/test_oracle.py): factor 1 is the plain table for every type;
+    linear scaling maps positions (s m, s n) to the plain scores at (m, n);
+    NTK keeps the fastest pair and divides the slowest by s; YaRN and llama3
+    keep fast pairs, divide slow pairs by s and are monotone between; YaRN's
+    amplitude at s = e is 1.1.
+    """
+    theta = rope_theta(head_dim, base)
+    if scaling is None or scaling.get("type", "none") == "none":
+        return theta, 1.0
+    kind = scaling["type"]
+    f = float(scaling["factor"])
+    D = head_dim
+    if kind == "linear":
+        return theta / f, 1.0
+    if kind == "ntk":
+        return rope_theta(D, base * f ** (D / (D - 2.0))), 1.0
+    if kind == "yarn":
+        L = float(scaling["original_max_pos"])
+        bf, bs = float(scaling.get("beta_fast", 32.0)), float(scaling.get("beta_slow", 1.0))
+
+        def pair_index(rotations):  # pair whose rotations over L equal `rotations`
+            return D * np.log(L / (rotations * 2.0 * np.pi)) / (2.0 * np.log(base))
+
+        lo = max(np.floor(pair_index(bf)), 0.0)
+        hi = min(np.ceil(pair_index(bs)), D / 2 - 1.0)
+        if lo == hi:
+            hi += 0.001
+        ramp = np.clip((np.arange(D // 2) - lo) / (hi - lo), 0.0, 1.0)
+        th = theta / f * ramp + theta * (1.0 - ramp)
+        af = float(scaling.get("attn_factor", 0.0)) or (0.1 * np.log(f) + 1.0 if f > 1 else 1.0)
+        return th, af
+    if kind == "llama3":
+        L = float(scaling["original_max_pos"])
+        lo_f, hi_f = float(scaling["low_freq_factor"]), float(scaling["high_freq_factor"])
+        wl = 2.0 * np.pi / theta
+        smooth = np.clip((L / wl - lo_f) / (hi_f - lo_f), 0.0, 1.0)
+        th = np.where(wl < L / hi_f, theta,
+                      np.where(wl > L / lo_f, theta / f, (1 - smooth) * theta / f + smooth * theta))
+        return th, 1.0
+    raise ValueError(f"unknown RoPE scaling {kind!r}")
 
 
 def alibi_slopes(num_heads: int) -> np.ndarray:
@@ -146,15 +209,15 @@ def _segment_starts(segments) -> np.ndarray:
     return np.concatenate(parts) if parts else np.zeros(0, np.int64)
 
 
-def _encode_keys(K, pos, segments, theta, doc_local, pairing="half"):
+def _encode_keys(K, pos, segments, theta, doc_local, pairing="half", amp=1.0):
     """Keys encoded at their logical positions.
 
     Position-free pool: R_p k.  Document-local pool (stored R_t k): R_s of the
     stored key, s = the segment's start, which is R_{s+t} k.
     """
     if doc_local:
-        return rope_rotate(K, _segment_starts(segments), theta, pairing)
-    return rope_rotate(K, pos, theta, pairing)
+        return rope_rotate(K, _segment_starts(segments), theta, pairing, amp)
+    return rope_rotate(K, pos, theta, pairing, amp)
 
 
 def store_kv(k, v, slots, rope_pos, k_pool, v_pool, *, block_size, theta, pairing="half"):
@@ -204,7 +267,7 @@ def _softmax_attend(scores: np.ndarray, V: np.ndarray):
 
 def attention_decode(q, q_pos, segments, k_pool, v_pool, *, block_size, num_kv_heads,
                      theta, scale, rotate=True, doc_local=False, pairing="half",
-                     alibi=None):
+                     alibi=None, amp=1.0):
     """One decode query (all heads) of one request, eager RoPE.
 
     q: [Hq, D]; q_pos: the query's logical position m.  Keys are gathered,
@@ -215,7 +278,7 @@ def attention_decode(q, q_pos, segments, k_pool, v_pool, *, block_size, num_kv_h
     pairing selects the RoPE pairs (see rope_rotate).  alibi, an array of Hq
     slopes, replaces RoPE by the ALiBi score bias slope_h * (p - m) (§3.5
     "Score-space positional methods"; -slope times the distance for keys at
-    or before the query).
+    or before the query).  amp is the cos/sin amplitude of a scaled table.
     """
     qf = _as_f64(q)
     Hq, D = qf.shape
@@ -226,8 +289,8 @@ def attention_decode(q, q_pos, segments, k_pool, v_pool, *, block_size, num_kv_h
         K, V, pos, _ = gather_request(k_pool, v_pool, segments, block_size, g)
         qs = qf[g * G:(g + 1) * G]
         if rotate and alibi is None:
-            Kt = _encode_keys(K, pos, segments, theta, doc_local, pairing)
-            qt = rope_rotate(qs, np.full(G, q_pos), theta, pairing)
+            Kt = _encode_keys(K, pos, segments, theta, doc_local, pairing, amp)
+            qt = rope_rotate(qs, np.full(G, q_pos), theta, pairing, amp)
         else:
             Kt, qt = K, qs
         s = scale * (qt @ Kt.T)
@@ -265,7 +328,7 @@ def attention_decode_relative(q, q_pos, segments, k_pool, v_pool, *, block_size,
 
 def attention_prefill(q, q_pos0, segments, k_pool, v_pool, *, block_size, num_kv_heads,
                       theta, scale, rotate=True, rows=None, doc_local=False, pairing="half",
-                      alibi=None):
+                      alibi=None, amp=1.0):
     """New-token attention of one request, eager RoPE.
 
     q: [T, Hq, D]; new token j sits at position q_pos0 + j.  Keys of cached
@@ -273,7 +336,7 @@ def attention_prefill(q, q_pos0, segments, k_pool, v_pool, *, block_size, num_kv
     their position is <= the query's.  rows optionally restricts the query
     rows computed (sampled parity).  Returns out [T', Hq, D], lse [T', Hq].
     doc_local=True reads a document-local pool (stored keys R_t k);
-    pairing and alibi as for attention_decode.
+    pairing, alibi and amp as for attention_decode.
     """
     qf = _as_f64(q)
     T, Hq, D = qf.shape
@@ -285,12 +348,12 @@ def attention_prefill(q, q_pos0, segments, k_pool, v_pool, *, block_size, num_kv
     for g in range(num_kv_heads):
         K, V, pos, new = gather_request(k_pool, v_pool, segments, block_size, g)
         use_rope = rotate and alibi is None
-        Kt = _encode_keys(K, pos, segments, theta, doc_local, pairing) if use_rope else K
+        Kt = _encode_keys(K, pos, segments, theta, doc_local, pairing, amp) if use_rope else K
         visible = (~new)[None, :] | (pos[None, :] <= qpos[:, None])  # [T', n]
         for hh in range(G):
             h = g * G + hh
             qs = qf[rows, h, :]
-            qt = rope_rotate(qs, qpos, theta, pairing) if use_rope else qs
+            qt = rope_rotate(qs, qpos, theta, pairing, amp) if use_rope else qs
             s = scale * (qt @ Kt.T)
             if alibi is not None:
                 s = s + float(alibi[h]) * (pos[None, :] - qpos[:, None])
@@ -301,19 +364,16 @@ def attention_prefill(q, q_pos0, segments, k_pool, v_pool, *, block_size, num_kv
     return out, lse
 
 
-def _theta_of(w):
-    return rope_theta(w.head_dim, w.rope_base)
-
-
 def run_decode(w, requests=None, rotate=True, pools=None, doc_local=False, pairing="half",
-               alibi=None):
+               alibi=None, scaling=None):
     """Oracle outputs for decode workload w: {r: (out [Hq, D], lse [Hq])}.
 
     pools, if given, replaces (w.k_pool, w.v_pool), e.g. by a document-local
     pool written with store_kv (then doc_local=True).  pairing / alibi select
-    the positional encoding (see attention_decode).
+    the positional encoding (see attention_decode); scaling a scaled RoPE
+    table (see rope_theta_scaled).
     """
-    th = _theta_of(w)
+    th, amp = rope_theta_scaled(w.head_dim, w.rope_base, scaling)
     kp, vp = (w.k_pool, w.v_pool) if pools is None else pools
     reqs = range(w.batch) if requests is None else requests
     res = {}
@@ -321,18 +381,18 @@ def run_decode(w, requests=None, rotate=True, pools=None, doc_local=False, pairi
         res[r] = attention_decode(w.q[r], int(w.q_pos[r]), w.requests[r], kp, vp,
                                   block_size=w.block_size, num_kv_heads=w.num_kv_heads,
                                   theta=th, scale=w.scale, rotate=rotate, doc_local=doc_local,
-                                  pairing=pairing, alibi=alibi)
+                                  pairing=pairing, alibi=alibi, amp=amp)
     return res
 
 
 def run_prefill(w, requests=None, rows=None, rotate=True, pools=None, doc_local=False,
-                pairing="half", alibi=None):
+                pairing="half", alibi=None, scaling=None):
     """Oracle outputs for prefill workload w: {r: (out [T', Hq, D], lse [T', Hq])}.
 
     rows, if given, maps request -> array of new-token indices to compute;
-    pools / doc_local / pairing / alibi as for run_decode.
+    pools / doc_local / pairing / alibi / scaling as for run_decode.
     """
-    th = _theta_of(w)
+    th, amp = rope_theta_scaled(w.head_dim, w.rope_base, scaling)
     kp, vp = (w.k_pool, w.v_pool) if pools is None else pools
     reqs = range(w.batch) if requests is None else requests
     res = {}
@@ -342,5 +402,6 @@ def run_prefill(w, requests=None, rows=None, rotate=True, pools=None, doc_local=
         res[r] = attention_prefill(w.q[a:b], int(w.q_pos[r]), w.requests[r], kp, vp,
                                    block_size=w.block_size, num_kv_heads=w.num_kv_heads,
                                    theta=th, scale=w.scale, rotate=rotate, rows=rr,
-                                   doc_local=doc_local, pairing=pairing, alibi=alibi)
+                                   doc_local=doc_local, pairing=pairing, alibi=alibi,
+                                   amp=amp)
     return res

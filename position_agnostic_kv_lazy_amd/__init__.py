@@ -20,6 +20,9 @@ from .binding import (  # noqa: F401
     lazy_attn_status_string,
     lazy_attn_last_error,
     lazy_attn_rope_table,
+    lazy_attn_rope_table_scaled,
+    la_rope_scaling,
+    make_scaling,
     lazy_attn_alibi_slopes,
     lazy_attn_pack_segments,
     lazy_attn_validate_table,

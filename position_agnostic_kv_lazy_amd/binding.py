@@ -40,6 +40,7 @@ EXPORTED = (
     "lazy_attn_status_string",
     "lazy_attn_last_error",
     "lazy_attn_rope_table",
+    "lazy_attn_rope_table_scaled",
     "lazy_attn_alibi_slopes",
     "lazy_attn_pack_segments",
     "lazy_attn_validate_table",
@@ -68,6 +69,37 @@ class la_params(ctypes.Structure):
     ]
 
 
+class la_rope_scaling(ctypes.Structure):
+    _fields_ = [
+        ("type", ctypes.c_int32),
+        ("original_max_pos", ctypes.c_int32),
+        ("factor", ctypes.c_double),
+        ("low_freq_factor", ctypes.c_double),
+        ("high_freq_factor", ctypes.c_double),
+        ("beta_fast", ctypes.c_double),
+        ("beta_slow", ctypes.c_double),
+        ("attn_factor", ctypes.c_double),
+    ]
+
+
+SCALING_TYPES = {"none": 0, "linear": 1, "ntk": 2, "yarn": 3, "llama3": 4}
+
+
+def make_scaling(type="none", factor=1.0, original_max_pos=0, low_freq_factor=0.0,
+                 high_freq_factor=0.0, beta_fast=0.0, beta_slow=0.0,
+                 attn_factor=0.0) -> la_rope_scaling:
+    s = la_rope_scaling()
+    s.type = SCALING_TYPES.get(type, type)
+    s.original_max_pos = int(original_max_pos)
+    s.factor = float(factor)
+    s.low_freq_factor = float(low_freq_factor)
+    s.high_freq_factor = float(high_freq_factor)
+    s.beta_fast = float(beta_fast)
+    s.beta_slow = float(beta_slow)
+    s.attn_factor = float(attn_factor)
+    return s
+
+
 class LazyAttnError(RuntimeError):
     def __init__(self, status: int, func: str):
         self.status = status
@@ -90,6 +122,9 @@ _lib.lazy_attn_last_error.restype = ctypes.c_char_p
 _lib.lazy_attn_last_error.argtypes = []
 _lib.lazy_attn_rope_table.restype = ctypes.c_int
 _lib.lazy_attn_rope_table.argtypes = [ctypes.c_double, ctypes.c_int32, ctypes.c_int32, _f32p]
+_lib.lazy_attn_rope_table_scaled.restype = ctypes.c_int
+_lib.lazy_attn_rope_table_scaled.argtypes = [ctypes.c_double, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.POINTER(la_rope_scaling), _f32p]
 _lib.lazy_attn_alibi_slopes.restype = ctypes.c_int
 _lib.lazy_attn_alibi_slopes.argtypes = [ctypes.c_int32, _f32p]
 _lib.lazy_attn_pack_segments.restype = ctypes.c_int
@@ -166,6 +201,21 @@ def lazy_attn_rope_table(base: float, head_dim: int, rows: int) -> np.ndarray:
     out = np.empty((rows, head_dim), dtype=np.float32)
     _check(_lib.lazy_attn_rope_table(float(base), head_dim, rows,
                                      out.ctypes.data_as(_f32p)), "lazy_attn_rope_table")
+    return out
+
+
+def lazy_attn_rope_table_scaled(base: float, head_dim: int, rows: int, scaling=None) -> np.ndarray:
+    """Host float32 table [rows, head_dim] of a scaled RoPE variant.
+
+    scaling: None, a la_rope_scaling, or a dict of make_scaling arguments.
+    """
+    if isinstance(scaling, dict):
+        scaling = make_scaling(**scaling)
+    out = np.empty((rows, head_dim), dtype=np.float32)
+    ptr = None if scaling is None else ctypes.byref(scaling)
+    _check(_lib.lazy_attn_rope_table_scaled(float(base), head_dim, rows, ptr,
+                                            out.ctypes.data_as(_f32p)),
+           "lazy_attn_rope_table_scaled")
     return out
 
 

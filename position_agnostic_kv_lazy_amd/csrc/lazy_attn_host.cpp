@@ -2,6 +2,7 @@
 // table packing and validation, the cos/sin table, and kernel dispatch.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -164,7 +165,8 @@ LA_API const char* lazy_attn_status_string(la_status s) {
 
 LA_API const char* lazy_attn_last_error(void) { return g_last_error.c_str(); }
 
-LA_API la_status lazy_attn_rope_table(double base, int32_t head_dim, int32_t rows, float* out) {
+LA_API la_status lazy_attn_rope_table_scaled(double base, int32_t head_dim, int32_t rows,
+                                             const la_rope_scaling* sc, float* out) {
   try {
     if (out == nullptr) return fail(LA_ERR_INVALID_ARG, "out is NULL");
     if (!(base > 1.0) || !std::isfinite(base))
@@ -174,21 +176,81 @@ LA_API la_status lazy_attn_rope_table(double base, int32_t head_dim, int32_t row
     if (rows < 1 || rows > LA_MAX_POSITION)
       return fail(LA_ERR_INVALID_ARG, "rows must be in [1, 2^24], got %d", rows);
     const int half = head_dim / 2;
+    const double D = static_cast<double>(head_dim);
+    const int type = sc == nullptr ? LA_SCALING_NONE : sc->type;
+    const double f = sc == nullptr ? 1.0 : sc->factor;
+    if (type != LA_SCALING_NONE && !(f > 0.0 && std::isfinite(f)))
+      return fail(LA_ERR_INVALID_ARG, "scaling factor must be finite and > 0");
+    if ((type == LA_SCALING_YARN || type == LA_SCALING_LLAMA3) && sc->original_max_pos < 1)
+      return fail(LA_ERR_INVALID_ARG, "original_max_pos must be >= 1");
+    if (type == LA_SCALING_NTK && head_dim < 4)
+      return fail(LA_ERR_INVALID_ARG, "NTK scaling needs head_dim >= 4");
+    // theta_i, possibly with an NTK-adjusted base
+    const double b = type == LA_SCALING_NTK ? base * std::pow(f, D / (D - 2.0)) : base;
     std::vector<double> theta(half);
-    for (int i = 0; i < half; ++i)
-      theta[i] = std::pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(head_dim));
+    for (int i = 0; i < half; ++i) theta[i] = std::pow(b, -2.0 * i / D);
+    double amp = 1.0;
+    switch (type) {
+      case LA_SCALING_NONE:
+      case LA_SCALING_NTK:
+        break;
+      case LA_SCALING_LINEAR:
+        for (double& t : theta) t /= f;
+        break;
+      case LA_SCALING_YARN: {
+        const double L = sc->original_max_pos;
+        const double bf = sc->beta_fast > 0 ? sc->beta_fast : 32.0;
+        const double bs = sc->beta_slow > 0 ? sc->beta_slow : 1.0;
+        // the (fractional) pair index at which a pair turns `turns` times over L
+        auto index_of = [&](double turns) {
+          return D * std::log(L / (turns * 2.0 * M_PI)) / (2.0 * std::log(base));
+        };
+        const double lo = std::max(std::floor(index_of(bf)), 0.0);
+        double hi = std::min(std::ceil(index_of(bs)), static_cast<double>(half - 1));
+        if (hi == lo) hi += 0.001;
+        for (int i = 0; i < half; ++i) {
+          const double w = std::min(std::max((i - lo) / (hi - lo), 0.0), 1.0);  // 1 = interpolate
+          theta[i] = theta[i] * (1.0 - w) + theta[i] / f * w;
+        }
+        amp = sc->attn_factor > 0 ? sc->attn_factor : (f > 1.0 ? 0.1 * std::log(f) + 1.0 : 1.0);
+        break;
+      }
+      case LA_SCALING_LLAMA3: {
+        const double L = sc->original_max_pos;
+        const double lf = sc->low_freq_factor, hf = sc->high_freq_factor;
+        if (!(hf > lf) || !(lf > 0))
+          return fail(LA_ERR_INVALID_ARG, "llama3 scaling needs high_freq_factor > low_freq_factor > 0");
+        for (int i = 0; i < half; ++i) {
+          const double wavelen = 2.0 * M_PI / theta[i];
+          if (wavelen < L / hf) continue;  // fast pairs unchanged
+          if (wavelen > L / lf) {
+            theta[i] /= f;
+          } else {
+            const double t = (L / wavelen - lf) / (hf - lf);
+            theta[i] = (1.0 - t) * theta[i] / f + t * theta[i];
+          }
+        }
+        break;
+      }
+      default:
+        return fail(LA_ERR_INVALID_ARG, "unknown RoPE scaling type %d", type);
+    }
     for (int64_t pos = 0; pos < rows; ++pos) {
       float* row = out + pos * head_dim;
       for (int i = 0; i < half; ++i) {
         const double ang = static_cast<double>(pos) * theta[i];
-        row[i] = static_cast<float>(std::cos(ang));
-        row[half + i] = static_cast<float>(std::sin(ang));
+        row[i] = static_cast<float>(amp * std::cos(ang));
+        row[half + i] = static_cast<float>(amp * std::sin(ang));
       }
     }
     return ok();
   } catch (...) {
-    return fail(LA_ERR_INVALID_ARG, "unexpected exception in lazy_attn_rope_table");
+    return fail(LA_ERR_INVALID_ARG, "unexpected exception in lazy_attn_rope_table_scaled");
   }
+}
+
+LA_API la_status lazy_attn_rope_table(double base, int32_t head_dim, int32_t rows, float* out) {
+  return lazy_attn_rope_table_scaled(base, head_dim, rows, nullptr, out);
 }
 
 LA_API la_status lazy_attn_alibi_slopes(int32_t num_heads, float* out) {

@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -274,3 +274,35 @@ def test_pos_encoding_checks():
                                            4, 10)
     for enc in ("rope_half", "rope_interleaved", "alibi"):
         la.lazy_attn_decode_workspace_size(_params(pos_encoding=enc), 4, 10)
+
+
+@pytest.mark.parametrize("sc", [
+    {"type": "linear", "factor": 4.0},
+    {"type": "ntk", "factor": 4.0},
+    {"type": "yarn", "factor": 16.0, "original_max_pos": 4096, "beta_fast": 32.0, "beta_slow": 1.0},
+    {"type": "yarn", "factor": 4.0, "original_max_pos": 8192, "beta_fast": 32.0, "beta_slow": 1.0,
+     "attn_factor": 1.3},
+    {"type": "llama3", "factor": 8.0, "original_max_pos": 8192, "low_freq_factor": 1.0,
+     "high_freq_factor": 4.0},
+], ids=lambda d: d["type"])
+def test_scaled_table_matches_oracle(sc):
+    from oracle import rope_theta_scaled
+    D, rows, base = 128, 140000, 5e5
+    t = la.lazy_attn_rope_table_scaled(base, D, rows, sc)
+    th, amp = rope_theta_scaled(D, base, sc)
+    for p in (0, 1, 4097, 65535, 139999):
+        ang = p * th
+        np.testing.assert_allclose(t[p, :64], amp * np.cos(ang), atol=1.5e-7, rtol=0)
+        np.testing.assert_allclose(t[p, 64:], amp * np.sin(ang), atol=1.5e-7, rtol=0)
+
+
+def test_scaled_table_none_is_plain_table():
+    a = la.lazy_attn_rope_table(1e4, 64, 1000)
+    b = la.lazy_attn_rope_table_scaled(1e4, 64, 1000, None)
+    c = la.lazy_attn_rope_table_scaled(1e4, 64, 1000, {"type": "none"})
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(a, c)
+    with pytest.raises(la.LazyAttnError, match="factor"):
+        la.lazy_attn_rope_table_scaled(1e4, 64, 10, {"type": "linear", "factor": 0.0})
+    with pytest.raises(la.LazyAttnError, match="scaling type"):
+        la.lazy_attn_rope_table_scaled(1e4, 64, 10, {"type": 9, "factor": 2.0})

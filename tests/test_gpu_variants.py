@@ -143,3 +143,33 @@ def test_alibi_config3_prefill_sampled():
     a = int(w.cu_q[0])
     assert_parity(out[a + rows[0]], ref[0][0], "bf16", "cfg3/8 alibi prefill")
     assert_lse(lse[a + rows[0]], ref[0][1], "bf16", "cfg3/8 alibi prefill")
+
+
+_SCALED = [
+    {"type": "yarn", "factor": 16.0, "original_max_pos": 256, "beta_fast": 32.0, "beta_slow": 1.0},
+    {"type": "llama3", "factor": 8.0, "original_max_pos": 512, "low_freq_factor": 1.0,
+     "high_freq_factor": 4.0},
+    {"type": "ntk", "factor": 4.0},
+]
+
+
+@pytest.mark.parametrize("sc", _SCALED, ids=lambda d: d["type"])
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_scaled_rope_tables(sc, kind):
+    """Scaled / NTK / YaRN variants: only the cos/sin table changes (§3.5)."""
+    from position_agnostic_kv_lazy_amd import lazy_attn_rope_table_scaled
+    w = _tiny(kind, "bf16")
+    table = lazy_attn_rope_table_scaled(w.rope_base, w.head_dim, w.table_rows(), sc)
+    log(f"scaled table {sc['type']} {kind}")
+    out, lse, _ = Device(w).run(w, table=table)
+    if kind == "decode":
+        ref = run_decode(w, scaling=sc)
+        for r in range(w.batch):
+            assert_parity(out[r], ref[r][0], "bf16", f"{sc['type']} decode req {r}")
+            assert_lse(lse[r], ref[r][1], "bf16", f"{sc['type']} decode req {r}")
+    else:
+        ref = run_prefill(w, scaling=sc)
+        for r in range(w.batch):
+            a, b = int(w.cu_q[r]), int(w.cu_q[r + 1])
+            assert_parity(out[a:b], ref[r][0], "bf16", f"{sc['type']} prefill req {r}")
+            assert_lse(lse[a:b], ref[r][1], "bf16", f"{sc['type']} prefill req {r}")

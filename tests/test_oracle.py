@@ -656,3 +656,95 @@ def test_alibi_zero_slopes_is_unrotated_attention_and_shift_invariant():
     d = run_decode(w2, alibi=sl)
     for r in c:
         np.testing.assert_allclose(c[r][0], d[r][0], rtol=0, atol=1e-11)
+
+
+# ------------------------------------------------------ scaled RoPE tables
+_SCALINGS = [
+    {"type": "linear", "factor": 4.0},
+    {"type": "ntk", "factor": 4.0},
+    {"type": "yarn", "factor": 16.0, "original_max_pos": 4096, "beta_fast": 32.0,
+     "beta_slow": 1.0},
+    {"type": "llama3", "factor": 8.0, "original_max_pos": 8192, "low_freq_factor": 1.0,
+     "high_freq_factor": 4.0},
+]
+
+
+@pytest.mark.parametrize("sc", _SCALINGS, ids=lambda d: d["type"])
+def test_scaled_factor_one_is_plain(sc):
+    from oracle import rope_theta_scaled
+    th, amp = rope_theta_scaled(128, 5e5, dict(sc, factor=1.0))
+    np.testing.assert_allclose(th, rope_theta(128, 5e5), rtol=1e-14)
+    assert amp == 1.0
+
+
+@pytest.mark.parametrize("sc", _SCALINGS, ids=lambda d: d["type"])
+def test_scaled_tables_keep_fact_3_2(sc):
+    """Every variant is still a rotation: scores depend on n - m only (times amp^2)."""
+    from oracle import rope_theta_scaled
+    th, amp = rope_theta_scaled(64, 1e4, sc)
+    q, k = RNG.standard_normal(64), RNG.standard_normal(64)
+    for m, n in [(3, 9), (5000, 70000)]:
+        lhs = rope_rotate(q, m, th, amp=amp) @ rope_rotate(k, n, th, amp=amp)
+        rhs = amp * amp * (q @ rope_rotate(k, n - m, th))
+        assert abs(lhs - rhs) < 1e-9 * max(1.0, abs(rhs))
+
+
+def test_linear_scaling_is_position_interpolation():
+    """Positions s*p under linear scaling see the plain rotation at p."""
+    from oracle import rope_theta_scaled
+    th4, _ = rope_theta_scaled(64, 1e4, {"type": "linear", "factor": 4.0})
+    x = RNG.standard_normal((6, 64))
+    p = np.array([0, 1, 7, 100, 2048, 30000])
+    np.testing.assert_allclose(rope_rotate(x, 4 * p, th4), rope_rotate(x, p, rope_theta(64, 1e4)),
+                               rtol=0, atol=1e-9)
+
+
+def test_ntk_keeps_fastest_and_interpolates_slowest_pair():
+    from oracle import rope_theta_scaled
+    D, f = 128, 8.0
+    th, _ = rope_theta_scaled(D, 1e4, {"type": "ntk", "factor": f})
+    th0 = rope_theta(D, 1e4)
+    assert th[0] == th0[0] == 1.0
+    assert abs(th[-1] - th0[-1] / f) < 1e-15 * th0[-1] * 10
+    assert np.all(np.diff(th / th0) < 0)  # more interpolation the slower the pair
+
+
+def _rotations_over(L, th):
+    return L * th / (2 * np.pi)
+
+
+def test_yarn_ramp_follows_rotation_counts_and_attention_factor():
+    from oracle import rope_theta_scaled
+    D, base, L, s_ = 128, 1e4, 4096, 16.0
+    th0 = rope_theta(D, base)
+    th, amp = rope_theta_scaled(D, base, {"type": "yarn", "factor": s_, "original_max_pos": L,
+                                          "beta_fast": 32.0, "beta_slow": 1.0})
+    r = _rotations_over(L, th0)
+    step = base ** (2.0 / D)  # one pair index = this ratio in rotation count
+    fast = r > 32.0 * step
+    slow = r < 1.0 / step
+    assert fast.any() and slow.any()
+    np.testing.assert_allclose(th[fast], th0[fast], rtol=1e-15)
+    np.testing.assert_allclose(th[slow], th0[slow] / s_, rtol=1e-15)
+    ratio = th / th0
+    assert np.all(np.diff(ratio) <= 1e-15)  # monotone blend from 1 down to 1/s
+    assert abs(amp - (0.1 * math.log(s_) + 1.0)) < 1e-15
+    _, amp_e = rope_theta_scaled(D, base, {"type": "yarn", "factor": math.e,
+                                           "original_max_pos": L})
+    assert abs(amp_e - 1.1) < 1e-15
+
+
+def test_llama3_scaling_wavelength_classes():
+    from oracle import rope_theta_scaled
+    D, base, L = 128, 5e5, 8192
+    th0 = rope_theta(D, base)
+    th, amp = rope_theta_scaled(D, base, {"type": "llama3", "factor": 8.0, "original_max_pos": L,
+                                          "low_freq_factor": 1.0, "high_freq_factor": 4.0})
+    wl = 2 * np.pi / th0
+    keep, scaled = wl < L / 4.0, wl > L / 1.0
+    assert keep.any() and scaled.any() and (~keep & ~scaled).any()
+    np.testing.assert_allclose(th[keep], th0[keep], rtol=1e-15)
+    np.testing.assert_allclose(th[scaled], th0[scaled] / 8.0, rtol=1e-15)
+    mid = ~keep & ~scaled
+    assert np.all((th[mid] < th0[mid]) & (th[mid] > th0[mid] / 8.0))
+    assert amp == 1.0
