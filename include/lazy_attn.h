@@ -341,6 +341,31 @@ LA_API la_status lazy_attn_prefill(const la_params* p, const void* q, const void
                             const int32_t* q_pos0, const float* cos_sin, int32_t batch,
                             int32_t max_q_per_req, void* out, float* lse, void* stream);
 
+/*
+ * Document-cache simulator (host only; the hit-ratio model of §2, Eqs. 1-3
+ * and Table 1).  Replays n accesses (docs[i], pos[i]) -- document ids numbered
+ * by popularity rank (0 = most popular), prompt positions in
+ * [0, num_positions) -- against a cache of `capacity` entries and writes the
+ * number of hits to *hits.
+ *   policy    LA_CACHE_POSITION_AGNOSTIC: one entry per document (this
+ *             library's pool); LA_CACHE_POSITION_AWARE: one entry per
+ *             (document, position), as a position-encoded cache needs
+ *   eviction  LA_EVICT_LRU: least recently used entry evicted on a miss;
+ *             LA_EVICT_STATIC_TOP: the cache holds the most popular entries
+ *             and never changes (documents < capacity, or all positions of
+ *             documents < capacity / num_positions) -- Eqs. 1 and 2
+ * docs/pos are host arrays; pos may be NULL for the agnostic policy.
+ */
+typedef enum la_cache_policy {
+  LA_CACHE_POSITION_AGNOSTIC = 0,
+  LA_CACHE_POSITION_AWARE = 1
+} la_cache_policy;
+typedef enum la_cache_eviction { LA_EVICT_LRU = 0, LA_EVICT_STATIC_TOP = 1 } la_cache_eviction;
+
+LA_API la_status lazy_attn_cache_simulate(int64_t n, const int64_t* docs, const int32_t* pos,
+                                          int32_t num_positions, int64_t capacity,
+                                          int32_t policy, int32_t eviction, int64_t* hits);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -38,3 +38,4 @@ from .analysis import (  # noqa: F401
     decode_trigger_overhead,
     decode_overhead,
 )
+from .cache_oracle import simulate_cache  # noqa: F401,E402

@@ -30,4 +30,5 @@ from .binding import (  # noqa: F401
     lazy_attn_store_kv,
     lazy_attn_decode,
     lazy_attn_prefill,
+    lazy_attn_cache_simulate,
 )

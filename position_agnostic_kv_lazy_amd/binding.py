@@ -35,6 +35,8 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE_TOO_SMALL, LA_ER
 LA_BF16, LA_FP32 = 0, 1
 LA_POOL_POSITION_FREE, LA_POOL_DOC_LOCAL = 0, 1
 LA_ROPE_HALF, LA_ROPE_INTERLEAVED, LA_ALIBI = 0, 1, 2
+LA_CACHE_POSITION_AGNOSTIC, LA_CACHE_POSITION_AWARE = 0, 1
+LA_EVICT_LRU, LA_EVICT_STATIC_TOP = 0, 1
 
 EXPORTED = (
     "lazy_attn_status_string",
@@ -48,6 +50,7 @@ EXPORTED = (
     "lazy_attn_store_kv",
     "lazy_attn_decode",
     "lazy_attn_prefill",
+    "lazy_attn_cache_simulate",
 )
 
 
@@ -140,6 +143,9 @@ _lib.lazy_attn_store_kv.argtypes = [_prm, _P, _P, ctypes.c_int64, _P, _P, _P, _P
 _lib.lazy_attn_decode.restype = ctypes.c_int
 _lib.lazy_attn_decode.argtypes = [_prm, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                   _P, _P, _P, ctypes.c_size_t, _P]
+_lib.lazy_attn_cache_simulate.restype = ctypes.c_int
+_lib.lazy_attn_cache_simulate.argtypes = [ctypes.c_int64, _i64p, _i32p, ctypes.c_int32,
+                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _i64p]
 _lib.lazy_attn_prefill.restype = ctypes.c_int
 _lib.lazy_attn_prefill.argtypes = [_prm, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                    ctypes.c_int32, _P, _P, _P]
@@ -309,3 +315,19 @@ def lazy_attn_prefill(params: la_params, q, k_pool, v_pool, blk_words, req_blk_s
                                   _ptr(blk_words), _ptr(req_blk_start), _ptr(cu_q), _ptr(q_pos0),
                                   _ptr(cos_sin), batch, max_q_per_req, _ptr(out), _ptr(lse),
                                   _stream(stream)), "lazy_attn_prefill")
+
+
+def lazy_attn_cache_simulate(docs, pos, num_positions: int, capacity: int, policy="agnostic",
+                             eviction="lru") -> int:
+    """Hits of a document-cache access trace (host arrays); see the C header."""
+    d = np.ascontiguousarray(docs, dtype=np.int64)
+    p = None if pos is None else np.ascontiguousarray(pos, dtype=np.int32)
+    pol = {"agnostic": LA_CACHE_POSITION_AGNOSTIC, "aware": LA_CACHE_POSITION_AWARE}.get(policy,
+                                                                                         policy)
+    ev = {"lru": LA_EVICT_LRU, "static_top": LA_EVICT_STATIC_TOP}.get(eviction, eviction)
+    hits = ctypes.c_int64(0)
+    _check(_lib.lazy_attn_cache_simulate(len(d), d.ctypes.data_as(_i64p),
+                                         None if p is None else p.ctypes.data_as(_i32p),
+                                         int(num_positions), int(capacity), pol, ev,
+                                         ctypes.byref(hits)), "lazy_attn_cache_simulate")
+    return int(hits.value)

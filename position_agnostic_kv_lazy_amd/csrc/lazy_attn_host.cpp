@@ -8,11 +8,17 @@
 #include <cstdio>
 #include <climits>
 #include <cstring>
+#include <new>
 #include <string>
 #include <vector>
 
 #include "lazy_attn.h"
 #include "launch.hpp"
+
+namespace lazyattn {
+int64_t simulate_cache(int64_t n, const int64_t* docs, const int32_t* pos, int64_t capacity,
+                       int policy, int eviction, int32_t num_positions);
+}  // namespace lazyattn
 
 namespace {
 
@@ -506,6 +512,38 @@ LA_API la_status lazy_attn_prefill(const la_params* p, const void* q, const void
     return ok();
   } catch (...) {
     return fail(LA_ERR_HIP, "unexpected exception in lazy_attn_prefill");
+  }
+}
+
+LA_API la_status lazy_attn_cache_simulate(int64_t n, const int64_t* docs, const int32_t* pos,
+                                          int32_t num_positions, int64_t capacity,
+                                          int32_t policy, int32_t eviction, int64_t* hits) {
+  try {
+    if (hits == nullptr) return fail(LA_ERR_INVALID_ARG, "hits is NULL");
+    if (n < 0 || capacity < 0) return fail(LA_ERR_INVALID_ARG, "n and capacity must be >= 0");
+    if (policy != LA_CACHE_POSITION_AGNOSTIC && policy != LA_CACHE_POSITION_AWARE)
+      return fail(LA_ERR_INVALID_ARG, "unknown cache policy %d", policy);
+    if (eviction != LA_EVICT_LRU && eviction != LA_EVICT_STATIC_TOP)
+      return fail(LA_ERR_INVALID_ARG, "unknown eviction %d", eviction);
+    if (num_positions < 1 || num_positions > 65536)
+      return fail(LA_ERR_INVALID_ARG, "num_positions must be in [1, 65536]");
+    if (n > 0 && docs == nullptr) return fail(LA_ERR_INVALID_ARG, "docs is NULL");
+    const bool need_pos = policy == LA_CACHE_POSITION_AWARE;
+    if (n > 0 && need_pos && pos == nullptr) return fail(LA_ERR_INVALID_ARG, "pos is NULL");
+    for (int64_t i = 0; i < n; ++i) {
+      if (docs[i] < 0 || docs[i] > (INT64_MAX / 65536))
+        return fail(LA_ERR_INVALID_ARG, "access %lld: document id %lld out of range", (long long)i,
+                    (long long)docs[i]);
+      if (need_pos && (pos[i] < 0 || pos[i] >= num_positions))
+        return fail(LA_ERR_INVALID_ARG, "access %lld: position %d outside [0, %d)", (long long)i,
+                    pos[i], num_positions);
+    }
+    *hits = lazyattn::simulate_cache(n, docs, pos, capacity, policy, eviction, num_positions);
+    return ok();
+  } catch (const std::bad_alloc&) {
+    return fail(LA_ERR_INVALID_ARG, "out of host memory in lazy_attn_cache_simulate");
+  } catch (...) {
+    return fail(LA_ERR_INVALID_ARG, "unexpected exception in lazy_attn_cache_simulate");
   }
 }
 

@@ -14,6 +14,7 @@ from .synth import (  # noqa: F401
     make_config,
     build_workload,
     segment_writes,
+    doc_trace,
     segment_slots,
     private_copies,
     zipf_probs,

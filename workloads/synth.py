@@ -39,6 +39,7 @@ __all__ = [
     "MixedWorkload",
     "CONFIGS",
     "segment_writes",
+    "doc_trace",
     "segment_slots",
     "private_copies",
     "make_config",
@@ -535,3 +536,40 @@ def segment_writes(w, positions: str = "index"):
             ps.append(t if positions == "index" else int(seg.start) + t)
     return (np.ascontiguousarray(np.concatenate(ks)), np.ascontiguousarray(np.concatenate(vs)),
             np.concatenate(sl).astype(np.int64), np.concatenate(ps).astype(np.int32))
+
+
+def doc_trace(n_queries: int, num_docs: int, alpha: float, docs_per_query: int, seed: int):
+    """Document accesses of a RAG query stream (the §2 / Table 1 workload shape).
+
+    Each query retrieves docs_per_query distinct documents drawn with Zipf
+    popularity p(d) ~ (d+1)^-alpha (d = popularity rank), in random order; a
+    document's prompt position is its slot in the query (0 .. K-1), so it may
+    appear at D = docs_per_query positions.  Returns (docs int64, pos int32),
+    one entry per access, query after query.  Pure sampling.
+    """
+    rng = np.random.default_rng([3000, seed])
+    cdf = np.cumsum(zipf_probs(num_docs, alpha))
+    K = docs_per_query
+    if K > num_docs:
+        raise ValueError("more documents per query than documents")
+
+    def draws(n):  # inverse-CDF Zipf samples
+        return np.minimum(np.searchsorted(cdf, rng.random(n), side="right"), num_docs - 1)
+
+    docs = np.empty((n_queries, K), np.int64)
+    stream = draws(4 * K * n_queries + 64).tolist()
+    at = 0
+    for qi in range(n_queries):
+        row, seen = [], set()
+        while len(row) < K:  # distinct documents per query
+            if at == len(stream):
+                stream, at = draws(4 * K + 64).tolist(), 0
+            d = stream[at]
+            at += 1
+            if d not in seen:
+                seen.add(d)
+                row.append(d)
+        docs[qi] = row
+    docs = rng.permuted(docs, axis=1)
+    pos = np.broadcast_to(np.arange(K, dtype=np.int32), (n_queries, K))
+    return docs.ravel(), np.ascontiguousarray(pos).ravel()
