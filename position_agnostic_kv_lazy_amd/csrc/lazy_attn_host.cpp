@@ -43,6 +43,11 @@ la_status hip_fail(hipError_t e, const char* what) {
   return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Launch errors are read with hipGetLastError, which also returns an error an
+// earlier, unrelated HIP call of the caller left on this thread; consume it
+// first so a launch reports only its own failure.
+void clear_stale_hip_error() { (void)hipGetLastError(); }
+
 constexpr int kBf16HeadDim = 128;
 constexpr int kBf16BlockSize = 16;
 
@@ -442,6 +447,7 @@ LA_API la_status lazy_attn_store_kv(const la_params* p, const void* k, const voi
     for (const void* ptr : {k, v, static_cast<const void*>(k_pool), static_cast<const void*>(v_pool)})
       if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
         return fail(LA_ERR_INVALID_ARG, "k, v, k_pool and v_pool must be 16-byte aligned");
+    clear_stale_hip_error();
     const hipError_t e = lazyattn::launch_store_kv(
         k, v, n_tokens, slots, rope_pos, cos_sin, p->num_kv_heads, p->head_dim, p->block_size,
         p->dtype == LA_BF16, p->pos_encoding == LA_ROPE_INTERLEAVED, k_pool, v_pool,
@@ -469,6 +475,7 @@ LA_API la_status lazy_attn_decode(const la_params* p, const void* q, const void*
     const lazyattn::AttnArgs a = make_args(p, q, k_pool, v_pool, blk_words, req_blk_start, nullptr,
                                            q_pos, cos_sin, batch, 1, max_blocks_per_req, out, lse);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    clear_stale_hip_error();
     hipError_t e;
     if (p->dtype == LA_FP32) {
       e = lazyattn::launch_attn_f32(a, false, s);
@@ -506,6 +513,7 @@ LA_API la_status lazy_attn_prefill(const la_params* p, const void* q, const void
     const lazyattn::AttnArgs a = make_args(p, q, k_pool, v_pool, blk_words, req_blk_start, cu_q,
                                            q_pos0, cos_sin, batch, max_q_per_req, 0, out, lse);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    clear_stale_hip_error();
     const hipError_t e = p->dtype == LA_FP32 ? lazyattn::launch_attn_f32(a, true, s)
                                              : lazyattn::launch_prefill_bf16(a, s);
     if (e != hipSuccess) return hip_fail(e, "lazy_attn_prefill launch");

@@ -128,3 +128,20 @@ def test_config5_fp32_mode_sampled():
     rows = {0: np.array([0, 1, 63, 64, 127])}
     rp = run_prefill(m.prefill, requests=[0], rows=rows)
     assert_parity(op[rows[0]], rp[0][0], "f32", "cfg5-f32 prefill req 0")
+
+
+def test_stale_hip_error_is_not_reported():
+    """An unrelated failed HIP call left on the thread does not fail our launch."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch and the library share
+    w = _tiny("decode", "bf16")
+    k, v = upload_pool(w.k_pool, w.v_pool, "cuda")
+    db = prepare(w, k, v)
+    torch.cuda.synchronize()
+    n = ctypes.c_int(0)
+    assert hip.hipGetDeviceCount(ctypes.byref(n)) == 0
+    assert hip.hipSetDevice(n.value + 7) != 0  # invalid ordinal: a host-side error only
+    db.run()  # must not raise
+    torch.cuda.synchronize()
+    ref = run_decode(w)
+    assert_parity(db.out_f32()[0], ref[0][0], "bf16", "after a stale HIP error")
