@@ -10,6 +10,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "lazy_attn.h"
@@ -246,13 +247,32 @@ LA_API la_status lazy_attn_rope_table_scaled(double base, int32_t head_dim, int3
       default:
         return fail(LA_ERR_INVALID_ARG, "unknown RoPE scaling type %d", type);
     }
-    for (int64_t pos = 0; pos < rows; ++pos) {
-      float* row = out + pos * head_dim;
-      for (int i = 0; i < half; ++i) {
-        const double ang = static_cast<double>(pos) * theta[i];
-        row[i] = static_cast<float>(amp * std::cos(ang));
-        row[half + i] = static_cast<float>(amp * std::sin(ang));
+    // Rows are independent (no incremental rotation, so no error accumulates
+    // along positions): split them over host threads.
+    auto fill = [&](int64_t r0, int64_t r1) {
+      for (int64_t pos = r0; pos < r1; ++pos) {
+        float* row = out + pos * head_dim;
+        for (int i = 0; i < half; ++i) {
+          const double ang = static_cast<double>(pos) * theta[i];
+          row[i] = static_cast<float>(amp * std::cos(ang));
+          row[half + i] = static_cast<float>(amp * std::sin(ang));
+        }
       }
+    };
+    const int64_t work = static_cast<int64_t>(rows) * half;
+    unsigned nt = std::thread::hardware_concurrency();
+    nt = std::max(1u, std::min(nt, 32u));
+    if (work < (int64_t{1} << 18)) nt = 1;
+    if (nt == 1) {
+      fill(0, rows);
+    } else {
+      std::vector<std::thread> pool;
+      const int64_t step = (rows + nt - 1) / nt;
+      for (unsigned t = 0; t < nt; ++t) {
+        const int64_t r0 = t * step, r1 = std::min<int64_t>(rows, r0 + step);
+        if (r0 < r1) pool.emplace_back(fill, r0, r1);
+      }
+      for (auto& th : pool) th.join();
     }
     return ok();
   } catch (...) {

@@ -145,3 +145,30 @@ def test_stale_hip_error_is_not_reported():
     torch.cuda.synchronize()
     ref = run_decode(w)
     assert_parity(db.out_f32()[0], ref[0][0], "bf16", "after a stale HIP error")
+
+
+def test_positions_at_the_24_bit_limit():
+    """Keys and queries up to position 2^24 - 1, the largest the block word encodes (fp32 mode)."""
+    import time
+    top = (1 << 24) - 1
+    dreq = [[("doc", 0, top - 700), ("doc", 1, 5), ("doc", 2, top - 64)]]
+    wd = build_workload(name="lim", kind="decode", dtype="f32", num_q_heads=4, num_kv_heads=2,
+                        head_dim=64, block_size=16, rope_base=1e4, doc_lens=[48, 37, 64],
+                        requests=dreq, seed=3, q_pos_override=[top])
+    preq = [[("doc", 0, top - 700), ("new", 40, top - 39)]]
+    wp = build_workload(name="lim", kind="prefill", dtype="f32", num_q_heads=4, num_kv_heads=2,
+                        head_dim=64, block_size=16, rope_base=1e4, doc_lens=[48, 37, 64],
+                        requests=preq, seed=3)
+    assert wd.table_rows() == 1 << 24 and wp.table_rows() == 1 << 24
+    t0 = time.time()
+    from position_agnostic_kv_lazy_amd import lazy_attn_rope_table
+    table = lazy_attn_rope_table(wd.rope_base, wd.head_dim, 1 << 24)
+    log(f"2^24-row table built in {time.time() - t0:.1f} s")
+    od, ld, _ = Device(wd).run(wd, table=table)
+    rd = run_decode(wd)
+    assert_parity(od[0], rd[0][0], "f32", "decode at 2^24 - 1")
+    assert_lse(ld[0], rd[0][1], "f32", "decode at 2^24 - 1")
+    op, lp, _ = Device(wp).run(wp, table=table)
+    rp = run_prefill(wp)
+    assert_parity(op, rp[0][0], "f32", "prefill ending at 2^24 - 1")
+    assert_lse(lp, rp[0][1], "f32", "prefill ending at 2^24 - 1")
