@@ -11,7 +11,11 @@
 // a q tile is 256 MFMA rows = (256 / G) new tokens x the G query heads of the
 // kv head, so the GQA group shares every staged K/V tile and the rotation of a
 // key is amortised over 256 query rows.  Wave w owns rows 32w .. 32w+31.
-// Per 64-key tile (4 blocks), double-buffered in LDS:
+// Per 64-key tile (4 blocks), double-buffered in LDS.  Staging runs two tiles
+// ahead and hides behind the MFMAs: while the S MFMAs of tile t execute, each
+// wave rotates and stores its keys of tile t+1 (loaded one iteration earlier)
+// into the other buffer and issues the key loads of tile t+2; while the P.V
+// MFMAs execute it does the same for the values.
 //   S'^T[64 keys x 32 rows]  = K' Q^T - m   18 x v_mfma_f32_32x32x16_bf16
 //   O^T[128 dims x 32 rows] += V^T P^T      16 x v_mfma_f32_32x32x16_bf16
 // The softmax reference -m of each row rides in the S product as one extra
@@ -210,7 +214,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
   const int vrem = tid & 255;
   const uint32_t v_off = static_cast<uint32_t>((vrem >> 1) * BS + 8 * (vrem & 1));
 
-  auto load_tile = [&](int tb, Staged& st) {
+  auto load_k = [&](int tb, Staged& st) {
     st.k1 = st.k2 = uint4{0u, 0u, 0u, 0u};
     const float* row = cs + 8 * cp;  // row 0 for blocks past the end
     if (tb + kblk < rb1) {
@@ -239,6 +243,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     } else {
       st.c0 = st.c1 = st.s0 = st.s1 = float4{0.f, 0.f, 0.f, 0.f};
     }
+  };
+
+  auto load_v = [&](int tb, Staged& st) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int vb = 2 * u + (wave_u >> 2);
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     }
   };
 
-  auto store_tile = [&](const Staged& st, int buf) {
+  auto store_k = [&](const Staged& st, int buf) {
     const float cc[8] = {st.c0.x, st.c0.y, st.c0.z, st.c0.w, st.c1.x, st.c1.y, st.c1.z, st.c1.w};
     const float ss[8] = {st.s0.x, st.s0.y, st.s0.z, st.s0.w, st.s1.x, st.s1.y, st.s1.z, st.s1.w};
     const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&st.k1);
@@ -285,6 +292,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     }
     *reinterpret_cast<uint4*>(&k_lds[buf][k_lds_off(kk, cp)]) = o1;
     *reinterpret_cast<uint4*>(&k_lds[buf][k_lds_off(kk, cp + 8)]) = o2;
+  };
+
+  auto store_v = [&](const Staged& st, int buf) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int vb = 2 * u + (wave_u >> 2);
@@ -309,8 +319,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
   const int ntiles = (rb1 - rb0 + BPT - 1) / BPT;
   Staged st;
   if (ntiles > 0) {
-    load_tile(rb0, st);
-    store_tile(st, 0);
+    load_k(rb0, st);
+    load_v(rb0, st);
+    store_k(st, 0);
+    store_v(st, 0);
+    if (ntiles > 1) {
+      load_k(rb0 + BPT, st);
+      load_v(rb0 + BPT, st);
+    }
   }
   __syncthreads();
 
@@ -318,7 +334,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     const int tb = rb0 + it * BPT;
     const int buf = it & 1;
     const bool more = it + 1 < ntiles;
-    if (more) load_tile(tb + BPT, st);  // prefetch the next tile into registers
 
     // Tile metadata (uniform): up to 4 blocks; missing blocks have no valid keys.
     int t_nv[BPT], t_pos0[BPT];
@@ -353,6 +368,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
             *reinterpret_cast<const uint4*>(&k_lds[buf][k_lds_off(32 * tk + col, 2 * s + h2)]);
         sacc[tk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qb[s], sacc[tk], 0, 0, 0);
       }
+    // While the S MFMAs run: stage tile it + 1 (loaded one iteration ago) into
+    // the other buffer, then start the loads of tile it + 2.
+    if (more) {
+      store_k(st, buf ^ 1);
+      if (it + 2 < ntiles) load_k(tb + 2 * BPT, st);
+    }
     // sacc[tk][rr] = score(key 32tk + 8(rr/4) + 4h2 + rr%4, this lane's row) - mref
     if (ALIBI) {
       // + slope * (p - m); the key of sacc[tk][rr] is slot 8((rr/4)%2) + 4h2 + rr%4 of
@@ -445,7 +466,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
             *reinterpret_cast<const uint4*>(&v_lds[buf][v_lds_off(32 * t + col, 2 * u + h2)]);
         oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[u], oacc[t], 0, 0, 0);
       }
-    if (more) store_tile(st, buf ^ 1);
+    // While the P.V MFMAs run: V of tile it + 1, then the V loads of tile it + 2.
+    if (more) {
+      store_v(st, buf ^ 1);
+      if (it + 2 < ntiles) load_v(tb + 2 * BPT, st);
+    }
     __syncthreads();
   }
 
