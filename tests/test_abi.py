@@ -306,3 +306,23 @@ def test_scaled_table_none_is_plain_table():
         la.lazy_attn_rope_table_scaled(1e4, 64, 10, {"type": "linear", "factor": 0.0})
     with pytest.raises(la.LazyAttnError, match="scaling type"):
         la.lazy_attn_rope_table_scaled(1e4, 64, 10, {"type": 9, "factor": 2.0})
+
+
+def test_error_message_is_per_thread():
+    import threading
+    msgs = {}
+
+    def fail(tag, fn):
+        try:
+            fn()
+        except la.LazyAttnError:
+            pass
+        msgs[tag] = la.lazy_attn_last_error()
+
+    t1 = threading.Thread(target=fail, args=("a", lambda: la.lazy_attn_alibi_slopes(0)))
+    t1.start(); t1.join()
+    t2 = threading.Thread(target=fail, args=("b", lambda: la.lazy_attn_rope_table(1.0, 64, 4)))
+    t2.start(); t2.join()
+    assert "num_heads" in msgs["a"] and "base" in msgs["b"]
+    la.lazy_attn_alibi_slopes(4)
+    assert la.lazy_attn_last_error() == ""  # success clears this thread's message
