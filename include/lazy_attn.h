@@ -34,17 +34,22 @@
  *  two half-dimensions).  The score of a query at position m and a key at
  *  position p is scale * (R_m q)^T (R_p k) = scale * q^T R_{p-m} k (§3.2,
  *  Fact 3.2).  Query head h reads kv head h / (num_q_heads / num_kv_heads)
- *  (§3.5 "GQA/MQA").
+ *  (§3.5 "GQA/MQA").  This is the default (LA_ROPE_HALF); la_pos_encoding
+ *  below selects interleaved pairs or ALiBi instead.
  *
  * Data layouts (row-major, contiguous)
  * ------------------------------------
  *  k_pool   [num_blocks][num_kv_heads][block_size][head_dim]   un-rotated K
+ *           (LA_POOL_POSITION_FREE; see la_pool_mode and la_pos_encoding
+ *           for the other stored forms)
  *  v_pool   [num_blocks][num_kv_heads][head_dim][block_size]   V, dim-major
  *           inside each (block, kv head) tile, so the token axis -- the
  *           contraction axis of P.V -- is contiguous.
  *  cos_sin  float32 [max_pos][2][head_dim/2]: row p holds cos(p theta_i) then
- *           sin(p theta_i).  Build it with lazy_attn_rope_table (float64
- *           arithmetic, rounded once to float32).  Always float32.
+ *           sin(p theta_i).  Build it with lazy_attn_rope_table or
+ *           lazy_attn_rope_table_scaled (float64 arithmetic, rounded once to
+ *           float32).  Always float32.  With LA_ALIBI this argument carries
+ *           the per-head slopes instead.
  *  q / out  decode:  [batch][num_q_heads][head_dim]
  *           prefill: [total_q][num_q_heads][head_dim], rows cu_q[r] ..
  *           cu_q[r+1]-1 are request r's new tokens.
@@ -59,12 +64,14 @@
  *  blocks, in any order.  Each 64-bit word packs (§3.2 "Decoding": block id,
  *  offset and mask bit-packed into one 64-bit register):
  *     bits  0..31  physical block id
- *     bits 32..55  pos0: logical position of the block's slot 0
+ *     bits 32..55  pos0: logical position of the block's slot 0 (cached
+ *                  blocks of a LA_POOL_DOC_LOCAL pool: the segment start)
  *     bits 56..62  n_valid - 1: slots 0 .. n_valid-1 hold tokens
  *     bit  63      causal: the block holds new prompt tokens of a prefill
  *                  request; its key at position p is visible to a query at
  *                  position m only when p <= m.  Ignored by decode.
- *  Slot i of a block is the token at logical position pos0 + i.
+ *  Slot i of a block is the token at logical position pos0 + i (position-free
+ *  pools).
  */
 #ifndef LAZY_ATTN_H
 #define LAZY_ATTN_H
