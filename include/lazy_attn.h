@@ -105,8 +105,8 @@ typedef enum la_dtype { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
  *    kernels rotate every key at its logical position (deferred encoding,
  *    §3.1).  Block words carry pos0 = logical position of slot 0.
  *  LA_POOL_DOC_LOCAL: each key stored pre-rotated by its index t within its
- *    segment (R_t k, "indexing from position 0", §3.2 "Prefilling" and
- *    Example 3.1).  Words of cached (non-causal) blocks carry pos0 = the
+ *    segment (R_t k: each document's cache numbered from position 0, §3.2
+ *    "Prefilling" and Example 3.1).  Words of cached (non-causal) blocks carry pos0 = the
  *    segment's logical start s for every block of the segment, and the score
  *    (R_m q)^T (R_{s+t} k) is computed as (R_{m-s} q)^T (R_t k) in decode --
  *    one rotation of q per segment, none of the keys (§3.2 "Decoding",

@@ -748,3 +748,41 @@ def test_llama3_scaling_wavelength_classes():
     mid = ~keep & ~scaled
     assert np.all((th[mid] < th0[mid]) & (th[mid] > th0[mid] / 8.0))
     assert amp == 1.0
+
+
+def test_llama3_blend_is_continuous_at_band_edges():
+    """Inside the smooth band the ratio theta'/theta runs from 1 (fast edge) to 1/s (slow edge)."""
+    from oracle import rope_theta_scaled
+    D, base, L, s_ = 4096, 5e5, 8192, 8.0
+    th0 = rope_theta(D, base)
+    th, _ = rope_theta_scaled(D, base, {"type": "llama3", "factor": s_, "original_max_pos": L,
+                                        "low_freq_factor": 1.0, "high_freq_factor": 4.0})
+    wl = 2 * np.pi / th0
+    ratio = th / th0
+    fast_edge = (wl > L / 4.0) & (wl < L / 4.0 * 1.02)
+    slow_edge = (wl < L / 1.0) & (wl > L / 1.0 * 0.98)
+    assert fast_edge.any() and slow_edge.any()
+    assert np.all(np.abs(ratio[fast_edge] - 1.0) < 0.05)
+    assert np.all(np.abs(ratio[slow_edge] * s_ - 1.0) < 0.05)
+
+
+def test_interleaved_storage_order_through_attention():
+    """Keys written with interleaved pairing, read as half-split pairs with q split the same way,
+    give the interleaved RoPE attention of the raw keys (document-local and position-free)."""
+    from oracle import store_kv
+    from workloads import segment_writes
+    w = _tiny("decode", dtype="f32")
+    th = rope_theta(w.head_dim, w.rope_base)
+    k, v, slots, idx = segment_writes(w, "index")
+    zeros = np.zeros(w.k_pool.shape)
+    perm = np.concatenate([np.arange(0, w.head_dim, 2), np.arange(1, w.head_dim, 2)])
+    import copy
+    wq = copy.copy(w)
+    wq.q = w.q[..., perm]  # q read the way the kernels read it
+    want = run_decode(w, pairing="interleaved")
+    for rope_pos, doc_local in ((None, False), (idx, True)):
+        pools = store_kv(k, v, slots, rope_pos, zeros, zeros, block_size=w.block_size, theta=th,
+                         pairing="interleaved")
+        got = run_decode(wq, pools=pools, doc_local=doc_local)
+        for r in want:
+            np.testing.assert_allclose(got[r][0], want[r][0], rtol=0, atol=1e-12)
