@@ -347,6 +347,12 @@ def _extra_rotation_ablation(w, k, v, stream, steps, pf_out):
         "max_abs_diff_vs_position_free": diff}
     del kt, vt, km, vm
     torch.cuda.empty_cache()
+
+    # ---- ALiBi (score-space positional method, no rotation) on the position-free pool
+    db = prepare(w, k, v, pos_encoding="alibi", max_pos=rows)
+    _, ams, _, _ = time_launches(lambda: db.run(stream), steps, 3, stream)
+    res["alibi"] = {"decode_event_ms_mean": round(ams, 5),
+                    "decode_gbs_logical": round(nbytes / (ams * 1e-3) / 1e9, 1)}
     return res
 
 
