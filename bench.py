@@ -204,13 +204,17 @@ def _extra_prefill(stream, steps):
 def _extra_long_decode(stream, steps):
     from position_agnostic_kv_lazy_amd.prepare import upload_pool
     from workloads import make_config
-    log("long-context decode (16 requests x 64K keys)")
-    w4 = make_config(4)
-    k4, v4 = upload_pool(w4.k_pool, w4.v_pool)
-    r4 = run_decode_workload(w4, k4, v4, stream, steps, 3)
-    out = _clean(r4)
-    out["roofline"] = roofline_hbm(r4["logical_kv_bytes"], r4["event_ms_mean"], "decode", w4.name)
-    return {w4.name: out}
+    try:
+        log("long-context decode (16 requests x 64K keys)")
+        w4 = make_config(4)
+        k4, v4 = upload_pool(w4.k_pool, w4.v_pool)
+        r4 = run_decode_workload(w4, k4, v4, stream, steps, 3)
+        out = _clean(r4)
+        out["roofline"] = roofline_hbm(r4["logical_kv_bytes"], r4["event_ms_mean"], "decode",
+                                       w4.name)
+        return {w4.name: out}
+    except Exception as e:  # reported, never hidden
+        return {"long_decode": {"error": repr(e)}}
 
 
 def _extra_mixed(stream, steps):
@@ -403,9 +407,14 @@ def main():
         main_res = run_decode_workload(w, k, v, stream, args.steps, args.warmup, args.split_blocks)
         if not args.no_extra:
             log("rotation ablation: doc-local pool and materialised copies")
-            ablation = _extra_rotation_ablation(w, k, v, stream, max(5, args.steps // 2),
-                                                main_res["_db"].out.view(torch.bfloat16))
-            ablation["position_free_decode_event_ms_mean"] = round(main_res["event_ms_mean"], 5)
+            try:
+                ablation = _extra_rotation_ablation(w, k, v, stream, max(5, args.steps // 2),
+                                                    main_res["_db"].out.view(torch.bfloat16))
+                ablation["position_free_decode_event_ms_mean"] = round(main_res["event_ms_mean"],
+                                                                       5)
+            except Exception as e:  # reported, never hidden
+                ablation = {"error": repr(e)}
+            torch.cuda.empty_cache()
         ms = main_res["wall_ms_per_step"]
         value, unit = main_res["logical_kv_bytes"] / (ms * 1e-3) / 1e9, "GB/s"
         config["keys_per_request"] = int(w.keys_per_request()[0])
