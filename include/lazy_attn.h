@@ -158,7 +158,7 @@ typedef struct la_params {
   float scale;           /* multiplies q.k; usually 1/sqrt(head_dim) */
   int32_t max_pos;       /* rows of cos_sin; every position must be < max_pos */
   int32_t split_blocks;  /* decode: blocks per split group, 0 = automatic */
-  int32_t target_workgroups; /* decode split heuristic, 0 = 1024 (256 CUs x 4) */
+  int32_t target_workgroups; /* decode split heuristic, 0 = 512 (256 CUs x 2) */
   int32_t pool_mode;     /* la_pool_mode of k_pool (above) */
   int32_t pos_encoding;  /* la_pos_encoding (above) */
   int32_t reserved[3];   /* must be zero */

@@ -389,7 +389,12 @@ DecodeSplit choose_decode_split(int batch, int num_kv_heads, int max_blocks_per_
   if (split_blocks > 0) {
     s.group_blocks = split_blocks;
   } else {
-    const int target = target_workgroups > 0 ? target_workgroups : 1024;
+    // Default: one full wave of resident workgroups on MI355X -- 256 CUs x 2
+    // four-wave workgroups (the VGPR budget allows two waves per SIMD).  A
+    // partial second wave leaves CUs idle at the tail, and more groups add
+    // partials and a combine pass (measured: 512 beats 768 and 1024 on both
+    // the 64 x 5K and the 16 x 64K decode batches).
+    const int target = target_workgroups > 0 ? target_workgroups : 512;
     const long pairs = static_cast<long>(batch) * num_kv_heads;
     long want = (target + pairs - 1) / pairs;  // groups per pair to fill the chip
     // keep at least 8 blocks per wave (32 per 4-wave group)

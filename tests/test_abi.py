@@ -151,17 +151,21 @@ def test_fp32_mode_allows_head_dim_64():
 
 def test_workspace_size_formula():
     p = _params()
-    # cfg2 shape: 64 requests x 8 kv heads = 512 pairs, 324 blocks each
-    n = la.lazy_attn_decode_workspace_size(p, 64, 324)
-    groups = 2  # ceil(1024 / 512) groups per pair
-    assert n == 64 * 32 * groups * 130 * 4
-    # enough pairs to fill the target: one group, no workspace, no combine
-    assert la.lazy_attn_decode_workspace_size(p, 256, 324) == 0
+    # cfg2 shape: 64 requests x 8 kv heads = 512 pairs fill the default target of
+    # 512 workgroups: one group per pair, no workspace, no combine
+    assert la.lazy_attn_decode_workspace_size(p, 64, 324) == 0
+    # fewer pairs: 32 x 8 = 256 pairs -> 2 groups each
+    assert la.lazy_attn_decode_workspace_size(p, 32, 324) == 32 * 32 * 2 * 130 * 4
+    # an explicit target
+    p1 = _params(target_workgroups=1024)
+    assert la.lazy_attn_decode_workspace_size(p1, 64, 324) == 64 * 32 * 2 * 130 * 4
     # explicit split size
     p2 = _params(split_blocks=100)
     assert la.lazy_attn_decode_workspace_size(p2, 64, 324) == 64 * 32 * 4 * 130 * 4
-    # long context: 16 x 8 pairs, 4096 blocks -> 8 groups
-    assert la.lazy_attn_decode_workspace_size(p, 16, 4096) == 16 * 32 * 8 * 130 * 4
+    # long context: 16 x 8 pairs, 4096 blocks -> 4 groups
+    assert la.lazy_attn_decode_workspace_size(p, 16, 4096) == 16 * 32 * 4 * 130 * 4
+    # short requests cap the split: at least 32 blocks per group (8 per wave)
+    assert la.lazy_attn_decode_workspace_size(p, 1, 64) == 1 * 32 * 2 * 130 * 4
 
 
 def test_validate_table_host_arrays():
@@ -199,9 +203,11 @@ def test_null_pointers_rejected_before_launch():
 
 def test_workspace_too_small_rejected_before_launch():
     p = _params()
+    # 32 requests x 8 kv heads need 2 groups per pair, hence a workspace
+    assert la.lazy_attn_decode_workspace_size(p, 32, 324) > 0
     fake = 1 << 40  # never dereferenced: the size check fails first
     with pytest.raises(la.LazyAttnError, match="WORKSPACE_TOO_SMALL"):
-        la.lazy_attn_decode(p, fake, fake, fake, fake, fake, fake, fake, 64, 324, fake,
+        la.lazy_attn_decode(p, fake, fake, fake, fake, fake, fake, fake, 32, 324, fake,
                             None, None, None)
 
 
