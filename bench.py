@@ -125,12 +125,18 @@ def run_prefill_workload(w, k, v, stream, steps, warmup):
     }
 
 
-def roofline_hbm(nbytes, ms, kind, workload):
+def roofline_hbm(nbytes, ms, kind, workload, split):
+    """Decode roofline; `split` says whether the launch ran split groups (then a
+    combine kernel follows the decode kernel and both are timed)."""
     gbs = nbytes / (ms * 1e-3) / 1e9
+    traffic = traffic_for(kind, workload)
+    per_launch = {"algorithmic_bytes": nbytes, "avg_ms": round(ms, 5)}
+    if traffic is not None:  # measured DRAM bytes at the same rate: the real HBM load
+        per_launch["dram_gbs"] = round(traffic / (ms * 1e-3) / 1e9, 1)
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(kind, workload),
-            "kernel": "decode_bf16_kernel (+ decode_combine_kernel)",
-            "per_launch": {"algorithmic_bytes": nbytes, "avg_ms": round(ms, 5)}}
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "decode_bf16_kernel + decode_combine_kernel" if split else "decode_bf16_kernel",
+            "per_launch": per_launch}
 
 
 def roofline_mfma(flops, ms, kind, workload):
@@ -211,7 +217,7 @@ def _extra_long_decode(stream, steps):
         r4 = run_decode_workload(w4, k4, v4, stream, steps, 3)
         out = _clean(r4)
         out["roofline"] = roofline_hbm(r4["logical_kv_bytes"], r4["event_ms_mean"], "decode",
-                                       w4.name)
+                                       w4.name, r4["workspace_bytes"] > 0)
         return {w4.name: out}
     except Exception as e:  # reported, never hidden
         return {"long_decode": {"error": repr(e)}}
@@ -419,7 +425,7 @@ def main():
         value, unit = main_res["logical_kv_bytes"] / (ms * 1e-3) / 1e9, "GB/s"
         config["keys_per_request"] = int(w.keys_per_request()[0])
         roof = roofline_hbm(main_res["logical_kv_bytes"], main_res["event_ms_mean"], "decode",
-                            wl_name)
+                            wl_name, main_res["workspace_bytes"] > 0)
     else:
         log("timing headline prefill")
         main_res = run_prefill_workload(w, k, v, stream, args.steps, args.warmup)
