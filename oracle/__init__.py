@@ -9,10 +9,16 @@ Retrieval-Augmented Generation with Deferred Positional Encoding" (§3.1
 Eq. 4 and the RoPE form of attention, §3.2 Fact 3.2 and the rotation
 formula, §2 Eqs. 1-3, §3.1-§3.2 cost model).
 
-Pinned by tests/test_oracle.py (see each function's docstring for its pin).
-Parity unpinned: none of the pages print attention outputs, so beyond the
-invariants, special cases and brute force listed there, the oracle's outputs
-rest on the definition of RoPE attention itself.
+Every function is pinned by tests/test_oracle.py or tests/test_cache_sim.py
+to something other than itself (each docstring names its pin): closed forms
+(Eq. 3's 2.86x, Eqs. 1-2, the cost-model percentages), identities (Fact 3.2,
+lazy = eager, shift invariance), special cases that reduce to a library or
+textbook routine (identity table -> scaled dot-product attention, contiguous
+placement -> causal RoPE attention, published NTK/YaRN/Llama-3.1 and ALiBi
+formulas), and brute force in scalar Python on tiny inputs.  The pages print
+no attention outputs, so no pin is a worked example of the attention itself.
+The only result left unpinned is a reproduction of Table 1's cells: the pages
+state neither the document size nor the eviction policy behind them.
 """
 from .lazy_oracle import (  # noqa: F401
     rope_theta,
