@@ -93,7 +93,7 @@ def run_decode_workload(w, k, v, stream, steps, warmup, split_blocks=0):
     from position_agnostic_kv_lazy_amd.prepare import prepare
     db = prepare(w, k, v, split_blocks=split_blocks)
     run = lambda: db.run(stream)  # noqa: E731
-    wall, ev_mean, ev_med, _ = time_launches(run, steps, warmup, stream)
+    wall, ev_mean, ev_med, per = time_launches(run, steps, warmup, stream)
     _, cold_mean, cold_med, _ = time_launches(run, max(5, steps // 2), 1, stream, make_flusher())
     nbytes = w.logical_kv_bytes()
     return {
@@ -101,6 +101,8 @@ def run_decode_workload(w, k, v, stream, steps, warmup, split_blocks=0):
         "wall_ms_per_step": 1e3 * wall / steps,
         "event_ms_mean": ev_mean,
         "event_ms_median": ev_med,
+        "event_ms_p10": float(np.percentile(per, 10)),
+        "event_ms_p90": float(np.percentile(per, 90)),
         "gbs_logical": nbytes / (ev_mean * 1e-3) / 1e9,
         "cold_event_ms_mean": cold_mean,
         "cold_gbs_logical": nbytes / (cold_mean * 1e-3) / 1e9,
@@ -113,13 +115,15 @@ def run_prefill_workload(w, k, v, stream, steps, warmup):
     from position_agnostic_kv_lazy_amd.prepare import prepare
     db = prepare(w, k, v)
     run = lambda: db.run(stream)  # noqa: E731
-    wall, ev_mean, ev_med, _ = time_launches(run, steps, warmup, stream)
+    wall, ev_mean, ev_med, per = time_launches(run, steps, warmup, stream)
     flops = w.prefill_flops()
     return {
         "flops": flops,
         "wall_ms_per_step": 1e3 * wall / steps,
         "event_ms_mean": ev_mean,
         "event_ms_median": ev_med,
+        "event_ms_p10": float(np.percentile(per, 10)),
+        "event_ms_p90": float(np.percentile(per, 90)),
         "tflops": flops / (ev_mean * 1e-3) / 1e12,
         "_db": db,
     }
@@ -147,6 +151,17 @@ def roofline_mfma(flops, ms, kind, workload):
             "per_launch": {"algorithmic_flops": flops, "avg_ms": round(ms, 5)}}
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The fp64 oracle, as it stands, on a bounded sample of the headline workload.
 
@@ -169,7 +184,8 @@ def cpu_baseline(w, budget_s=12.0):
                 units += 1
             dt = time.perf_counter() - t0
             return {"value": round(work / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-                    "kind": "oracle",
+                    "kind": "oracle", "cpu_model": _cpu_model(),
+                    "visible_cores": len(os.sched_getaffinity(0)),
                     "sample": f"{units} decode requests (cycling over the {w.batch}-request "
                               f"batch), fp64 NumPy, BLAS limited to 1 thread, {dt:.1f} s"}
         cached = w.keys_per_request() - np.array([w.q_len(r) for r in range(w.batch)])
@@ -182,7 +198,8 @@ def cpu_baseline(w, budget_s=12.0):
             units += 1
         dt = time.perf_counter() - t0
         return {"value": round(work / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-                "kind": "oracle",
+                "kind": "oracle", "cpu_model": _cpu_model(),
+                "visible_cores": len(os.sched_getaffinity(0)),
                 "sample": f"{units} slices of 16 new-token rows, fp64 NumPy, BLAS limited to "
                           f"1 thread, {dt:.1f} s"}
 
@@ -190,6 +207,50 @@ def cpu_baseline(w, budget_s=12.0):
 def _clean(res):
     return {kk: (round(vv, 5) if isinstance(vv, float) else vv)
             for kk, vv in res.items() if not kk.startswith("_")}
+
+
+def _extra_no_sharing(stream, steps):
+    """Control for the shared-document mix: configuration 2's shapes with every
+    request reading its own documents, so logical bytes = unique bytes = what
+    DRAM must deliver."""
+    from position_agnostic_kv_lazy_amd.prepare import upload_pool
+    from workloads import make_no_sharing_decode
+    try:
+        log("no-sharing control (64 requests x 10 private documents)")
+        w = make_no_sharing_decode()
+        k, v = upload_pool(w.k_pool, w.v_pool)
+        res = run_decode_workload(w, k, v, stream, steps, 3)
+        out = _clean(res)
+        out["frac_of_hbm_peak"] = round(res["gbs_logical"] / HBM_PEAK_GBS, 4)
+        out["cold_frac_of_hbm_peak"] = round(res["cold_gbs_logical"] / HBM_PEAK_GBS, 4)
+        return {w.name: out}
+    except Exception as e:  # reported, never hidden
+        return {"no_sharing_control": {"error": repr(e)}}
+
+
+def _extra_achievable(stream):
+    """Reference rates measured on the same GPU in the same run: a plain 1 GiB
+    device copy (torch copy_) and a plain bf16 GEMM (torch.matmul, 8192^3)."""
+    import torch
+    try:
+        log("achievable references: 1 GiB copy, 8192^3 bf16 GEMM")
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        _, copy_ms, _, _ = time_launches(lambda: dst.copy_(src), 10, 3, stream)
+        del src, dst
+        n = 8192
+        a = torch.randn(n, n, device="cuda").to(torch.bfloat16).contiguous()
+        b = torch.randn(n, n, device="cuda").to(torch.bfloat16).contiguous()
+        c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+        _, gemm_ms, _, _ = time_launches(lambda: torch.matmul(a, b, out=c), 10, 3, stream)
+        del a, b, c
+        torch.cuda.empty_cache()
+        return {"achievable_references": {
+            "copy_1gib_gbs_moved": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
+            "gemm_bf16_8192_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "note": "plain copy reads + writes 1 GiB; GEMM through torch.matmul (hipBLASLt)"}}
+    except Exception as e:  # reported, never hidden
+        return {"achievable_references": {"error": repr(e)}}
 
 
 def _extra_prefill(stream, steps):
@@ -465,6 +526,11 @@ def main():
             extra.update(_extra_long_decode(stream, steps2))
             torch.cuda.empty_cache()
         extra.update(_extra_mixed(stream, steps2))
+        torch.cuda.empty_cache()
+        if args.config == 2:
+            extra.update(_extra_no_sharing(stream, steps2))
+            torch.cuda.empty_cache()
+        extra.update(_extra_achievable(stream))
     result["extra"] = extra
 
     if not args.no_cpu:

@@ -12,6 +12,7 @@ from .synth import (  # noqa: F401
     MixedWorkload,
     CONFIGS,
     make_config,
+    make_no_sharing_decode,
     build_workload,
     segment_writes,
     doc_trace,

@@ -43,6 +43,7 @@ __all__ = [
     "segment_slots",
     "private_copies",
     "make_config",
+    "make_no_sharing_decode",
     "build_workload",
     "zipf_probs",
     "f32_to_bf16_bits",
@@ -449,6 +450,28 @@ def make_config(cfg: int, *, dtype: Optional[str] = None, scale_down: int = 1):
                              shared_pool=(pre.k_pool, pre.v_pool, pre.meta["priv_base"]), **common)
         return MixedWorkload(name="mixed_step", decode=dec, prefill=pre)
     raise ValueError(f"unknown config {cfg}")
+
+
+def make_no_sharing_decode(*, dtype: Optional[str] = None, scale_down: int = 1):
+    """Configuration 2's shapes with no document shared between requests.
+
+    64 requests x 10 documents of 512 tokens + a 64-token question, as in
+    configuration 2, but request r reads its own documents 10r .. 10r+9 (in a
+    seeded random order), so no block is read twice in a launch and the
+    logical K+V bytes equal the unique bytes: a control for the cache-assisted
+    rate of the shared-document mix.
+    """
+    sd = max(1, int(scale_down))
+    B, per = max(1, 64 // sd), 10
+    rng = np.random.default_rng(2012)
+    specs = []
+    for r in range(B):
+        docs = rng.permutation(np.arange(per * r, per * (r + 1)))
+        specs.append([("doc", int(d)) for d in docs] + [("priv", 64)])
+    return build_workload(name="llama3_8b_decode_no_sharing", kind="decode",
+                          dtype=dtype or "bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                          block_size=16, rope_base=5e5, doc_lens=[512] * (per * B),
+                          requests=specs, seed=1012)
 
 
 def segment_slots(w, positions: str = "index"):
