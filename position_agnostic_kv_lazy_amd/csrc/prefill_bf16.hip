@@ -354,6 +354,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
       tile_simple = tile_simple && t_nv[b] == BS && !t_causal[b];
     }
 
+    // Both MFMA phases ask the scheduler for its MFMA / LDS-read interleave
+    // (strategy 1); measured about 2 % faster than the default order.
+    __builtin_amdgcn_iglp_opt(1);
     // ---- S'^T = K' Q^T - m for this wave's 32 rows x 64 keys
     // The two 32-key accumulators alternate, so consecutive MFMAs are independent.
     f32x16 sacc[2];
@@ -456,6 +459,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     }
     lrun += psum;
 
+    __builtin_amdgcn_iglp_opt(1);
     // ---- O^T += V^T P^T
     // The four output tiles alternate, so consecutive MFMAs are independent.
 #pragma unroll
