@@ -15,7 +15,9 @@
 // ahead and hides behind the MFMAs: while the S MFMAs of tile t execute, each
 // wave rotates and stores its keys of tile t+1 (loaded one iteration earlier)
 // into the other buffer and issues the key loads of tile t+2; while the P.V
-// MFMAs execute it does the same for the values.
+// MFMAs execute it does the same for the values.  Staging has no branches
+// (tiles past the end read the request's last block and are zeroed), so each
+// MFMA phase is one basic block the scheduler can interleave.
 //   S'^T[64 keys x 32 rows]  = K' Q^T - m   18 x v_mfma_f32_32x32x16_bf16
 //   O^T[128 dims x 32 rows] += V^T P^T      16 x v_mfma_f32_32x32x16_bf16
 // The softmax reference -m of each row rides in the S product as one extra
@@ -215,26 +217,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
   const uint32_t v_off = static_cast<uint32_t>((vrem >> 1) * BS + 8 * (vrem & 1));
 
   auto load_k = [&](int tb, Staged& st) {
-    st.k1 = st.k2 = uint4{0u, 0u, 0u, 0u};
-    const float* row = cs + 8 * cp;  // row 0 for blocks past the end
-    if (tb + kblk < rb1) {
-      const BlockWord w = unpack_word(words[tb + kblk]);
-      const uint16_t* kb = k_pool + (static_cast<size_t>(w.block_id) * Hkv + g) * (BS * D);
-      if (ALIBI) {
-        row = cs;  // no table: keys are not rotated
-      } else if (DOC_LOCAL) {
-        row = cs + static_cast<size_t>(w.causal ? p0 : w.pos0) * D + 8 * cp;
-      } else {
-        // unused slots keep K = 0 and read the table row of the block's last key
-        row = cs + static_cast<size_t>(w.pos0) * D +
-              static_cast<uint32_t>(min(kslot, w.n_valid - 1) * D + 8 * cp);
-      }
-      if (kslot < w.n_valid) {
-        const uint32_t off = static_cast<uint32_t>(kslot * D + 8 * cp);
-        st.k1 = *reinterpret_cast<const uint4*>(kb + off);
-        st.k2 = *reinterpret_cast<const uint4*>(kb + off + HALF);
-      }
+    // Branch-free: a block past the end reads the request's last block (valid
+    // memory) and is zeroed; unused slots are zeroed too.
+    const bool blk_ok = tb + kblk < rb1;
+    const BlockWord w = unpack_word(words[min(tb + kblk, rb1 - 1)]);
+    const uint16_t* kb = k_pool + (static_cast<size_t>(w.block_id) * Hkv + g) * (BS * D);
+    const float* row;
+    if (ALIBI) {
+      row = cs;  // no table: keys are not rotated
+    } else if (DOC_LOCAL) {
+      row = cs + static_cast<size_t>(w.causal ? p0 : w.pos0) * D + 8 * cp;
+    } else {
+      // unused slots keep K = 0 and read the table row of the block's last key
+      row = cs + static_cast<size_t>(w.pos0) * D +
+            static_cast<uint32_t>(min(kslot, w.n_valid - 1) * D + 8 * cp);
     }
+    const uint32_t off = static_cast<uint32_t>(min(kslot, w.n_valid - 1) * D + 8 * cp);
+    const uint4 k1 = *reinterpret_cast<const uint4*>(kb + off);
+    const uint4 k2 = *reinterpret_cast<const uint4*>(kb + off + HALF);
+    const bool keep = blk_ok && kslot < w.n_valid;
+    st.k1 = keep ? k1 : uint4{0u, 0u, 0u, 0u};
+    st.k2 = keep ? k2 : uint4{0u, 0u, 0u, 0u};
     if (!ALIBI) {
       st.c0 = *reinterpret_cast<const float4*>(row);
       st.c1 = *reinterpret_cast<const float4*>(row + 4);
@@ -249,22 +252,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int vb = 2 * u + (wave_u >> 2);
-      st.v[u] = uint4{0u, 0u, 0u, 0u};
-      if (tb + vb < rb1) {
-        const BlockWord w = unpack_word(words[tb + vb]);
-        const uint16_t* vbase = v_pool + (static_cast<size_t>(w.block_id) * Hkv + g) * (D * BS);
-        st.v[u] = *reinterpret_cast<const uint4*>(vbase + v_off);
-        // zero slots >= n_valid among 8half .. 8half+7 (unused slots may hold anything)
-        const int nv = w.n_valid - 8 * (vrem & 1);
-        if (w.n_valid < BS) {
-          uint32_t* pv = reinterpret_cast<uint32_t*>(&st.v[u]);
+      const bool blk_ok = tb + vb < rb1;
+      const BlockWord w = unpack_word(words[min(tb + vb, rb1 - 1)]);
+      const uint16_t* vbase = v_pool + (static_cast<size_t>(w.block_id) * Hkv + g) * (D * BS);
+      const uint4 x = *reinterpret_cast<const uint4*>(vbase + v_off);
+      // zero slots >= n_valid among 8half .. 8half+7 (unused slots may hold anything)
+      const int nv = blk_ok ? w.n_valid - 8 * (vrem & 1) : 0;
+      const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+      uint32_t ys[4];
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const uint32_t keep = (2 * x < nv ? 0x0000FFFFu : 0u) | (2 * x + 1 < nv ? 0xFFFF0000u : 0u);
-            pv[x] &= keep;
-          }
-        }
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t keep = (2 * e < nv ? 0x0000FFFFu : 0u) | (2 * e + 1 < nv ? 0xFFFF0000u : 0u);
+        ys[e] = xs[e] & keep;
       }
+      st.v[u] = uint4{ys[0], ys[1], ys[2], ys[3]};
     }
   };
 
@@ -333,7 +334,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
   for (int it = 0; it < ntiles; ++it) {
     const int tb = rb0 + it * BPT;
     const int buf = it & 1;
-    const bool more = it + 1 < ntiles;
 
     // Tile metadata (uniform): up to 4 blocks; missing blocks have no valid keys.
     int t_nv[BPT], t_pos0[BPT];
@@ -373,10 +373,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
       }
     // While the S MFMAs run: stage tile it + 1 (loaded one iteration ago) into
     // the other buffer, then start the loads of tile it + 2.
-    if (more) {
-      store_k(st, buf ^ 1);
-      if (it + 2 < ntiles) load_k(tb + 2 * BPT, st);
-    }
+    store_k(st, buf ^ 1);  // past the last tile: a buffer nobody reads
+    load_k(tb + 2 * BPT, st);
     // sacc[tk][rr] = score(key 32tk + 8(rr/4) + 4h2 + rr%4, this lane's row) - mref
     if (ALIBI) {
       // + slope * (p - m); the key of sacc[tk][rr] is slot 8((rr/4)%2) + 4h2 + rr%4 of
@@ -471,10 +469,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
         oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[u], oacc[t], 0, 0, 0);
       }
     // While the P.V MFMAs run: V of tile it + 1, then the V loads of tile it + 2.
-    if (more) {
-      store_v(st, buf ^ 1);
-      if (it + 2 < ntiles) load_v(tb + 2 * BPT, st);
-    }
+    store_v(st, buf ^ 1);
+    load_v(tb + 2 * BPT, st);
     __syncthreads();
   }
 
