@@ -12,6 +12,10 @@ The same run also measures (unless --no-extra) the prefill, long-context
 decode and mixed decode+prefill workloads, each against its roofline, and
 (unless --no-cpu) the fp64 CPU oracle on a bounded sample of the headline
 workload.  Prints ONE JSON line.
+
+W defaults to 500 untimed launches: this GPU reaches its steady clocks only
+after some tens of milliseconds of back-to-back work, and a decode launch
+takes 0.16 ms, so a 10-launch warm-up would time the ramp.
 """
 from __future__ import annotations
 
@@ -29,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode attn KV GB/s (% HBM peak) + prefill TFLOPS (% MFMA peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+WARM_S = 0.25               # minimum warm-up (seconds of launches) for the extra workloads
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 KERNEL_SRC = {
     "decode": os.path.join(ROOT, "position_agnostic_kv_lazy_amd", "csrc", "decode_bf16.hip"),
@@ -58,11 +63,23 @@ def traffic_for(kind, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_launches(run, steps, warmup, stream, flush=None):
-    """Warm up, then time exactly `steps` launches: wall clock and per-launch HIP events."""
+def time_launches(run, steps, warmup, stream, flush=None, min_warm_s=0.0):
+    """Warm up, then time exactly `steps` launches: wall clock and per-launch HIP events.
+
+    The GPU raises its clocks only after some tens of milliseconds of sustained
+    work (a 0.17 ms decode launch runs about 10 % slower for its first ~150
+    back-to-back launches), so steady-state figures need enough warm-up:
+    `warmup` launches, continued until at least `min_warm_s` seconds of them
+    have run.
+    """
     import torch
-    for _ in range(warmup):
+    t_warm = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t_warm < min_warm_s:
         run()
+        done += 1
+        if done % 50 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
@@ -89,11 +106,12 @@ def make_flusher(nbytes=1 << 30):
     return flush
 
 
-def run_decode_workload(w, k, v, stream, steps, warmup, split_blocks=0):
+def run_decode_workload(w, k, v, stream, steps, warmup, split_blocks=0, min_warm_s=WARM_S):
     from position_agnostic_kv_lazy_amd.prepare import prepare
     db = prepare(w, k, v, split_blocks=split_blocks)
     run = lambda: db.run(stream)  # noqa: E731
-    wall, ev_mean, ev_med, per = time_launches(run, steps, warmup, stream)
+    wall, ev_mean, ev_med, per = time_launches(run, steps, warmup, stream, min_warm_s=min_warm_s)
+    # right after the warm timing: the clocks are up, one warm-up launch suffices
     _, cold_mean, cold_med, _ = time_launches(run, max(5, steps // 2), 1, stream, make_flusher())
     nbytes = w.logical_kv_bytes()
     return {
@@ -111,11 +129,11 @@ def run_decode_workload(w, k, v, stream, steps, warmup, split_blocks=0):
     }
 
 
-def run_prefill_workload(w, k, v, stream, steps, warmup):
+def run_prefill_workload(w, k, v, stream, steps, warmup, min_warm_s=WARM_S):
     from position_agnostic_kv_lazy_amd.prepare import prepare
     db = prepare(w, k, v)
     run = lambda: db.run(stream)  # noqa: E731
-    wall, ev_mean, ev_med, per = time_launches(run, steps, warmup, stream)
+    wall, ev_mean, ev_med, per = time_launches(run, steps, warmup, stream, min_warm_s=min_warm_s)
     flops = w.prefill_flops()
     return {
         "flops": flops,
@@ -236,13 +254,15 @@ def _extra_achievable(stream):
         log("achievable references: 1 GiB copy, 8192^3 bf16 GEMM")
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
-        _, copy_ms, _, _ = time_launches(lambda: dst.copy_(src), 10, 3, stream)
+        _, copy_ms, _, _ = time_launches(lambda: dst.copy_(src), 10, 3, stream,
+                                         min_warm_s=WARM_S)
         del src, dst
         n = 8192
         a = torch.randn(n, n, device="cuda").to(torch.bfloat16).contiguous()
         b = torch.randn(n, n, device="cuda").to(torch.bfloat16).contiguous()
         c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
-        _, gemm_ms, _, _ = time_launches(lambda: torch.matmul(a, b, out=c), 10, 3, stream)
+        _, gemm_ms, _, _ = time_launches(lambda: torch.matmul(a, b, out=c), 10, 3, stream,
+                                         min_warm_s=WARM_S)
         del a, b, c
         torch.cuda.empty_cache()
         return {"achievable_references": {
@@ -312,10 +332,10 @@ def _extra_mixed(stream, steps):
             dp.run(stream)
             dd.run(stream)
 
-        _, p2, _, _ = time_launches(pair_two_streams, steps, 3, stream)
-        _, p1, _, _ = time_launches(pair_serial, steps, 3, stream)
-        _, dm, _, _ = time_launches(lambda: dd.run(stream), steps, 3, stream)
-        _, fm, _, _ = time_launches(lambda: dp.run(stream), steps, 3, stream)
+        _, p2, _, _ = time_launches(pair_two_streams, steps, 3, stream, min_warm_s=WARM_S)
+        _, p1, _, _ = time_launches(pair_serial, steps, 3, stream, min_warm_s=WARM_S)
+        _, dm, _, _ = time_launches(lambda: dd.run(stream), steps, 3, stream, min_warm_s=WARM_S)
+        _, fm, _, _ = time_launches(lambda: dp.run(stream), steps, 3, stream, min_warm_s=WARM_S)
         nb = m5.decode.logical_kv_bytes()
         fl = m5.prefill.prefill_flops()
         return {"mixed_step": {
@@ -370,7 +390,7 @@ def _extra_rotation_ablation(w, k, v, stream, steps, pf_out):
 
     def decode(wx, kd, vd):
         db = prepare(wx, kd, vd, pool_mode="doc_local", max_pos=rows)
-        _, ms, _, _ = time_launches(lambda: db.run(stream), steps, 3, stream)
+        _, ms, _, _ = time_launches(lambda: db.run(stream), steps, 3, stream, min_warm_s=WARM_S)
         torch.cuda.synchronize()
         diff = float((db.out.view(torch.bfloat16).float() - pos_free).abs().max())
         return db, ms, diff
@@ -382,7 +402,7 @@ def _extra_rotation_ablation(w, k, v, stream, steps, pf_out):
     kd, vd = torch.zeros_like(k), torch.zeros_like(v)
     p_w = params_for(w, int(k.shape[0]), rows)
     run_w = store(p_w, kt, vt, slots, idx, kd, vd)
-    _, wms, _, _ = time_launches(run_w, max(3, steps // 4), 1, stream)
+    _, wms, _, _ = time_launches(run_w, max(3, steps // 4), 1, stream, min_warm_s=WARM_S)
     moved = 4 * len(slots) * Hkv * D * 2
     _, dms, diff = decode(w, kd, vd)
     res["doc_local"] = {
@@ -402,7 +422,7 @@ def _extra_rotation_ablation(w, k, v, stream, steps, pf_out):
     vm = torch.zeros((nb_m,) + tuple(v.shape[1:]), dtype=v.dtype, device=v.device)
     p_m = params_for(w, nb_m, rows)
     run_m = store(p_m, kt, vt, dst, pos, km, vm)
-    _, mms, _, _ = time_launches(run_m, max(3, steps // 4), 1, stream)
+    _, mms, _, _ = time_launches(run_m, max(3, steps // 4), 1, stream, min_warm_s=WARM_S)
     moved = 4 * len(dst) * Hkv * D * 2
     import copy
     wm = copy.copy(w)
@@ -421,7 +441,7 @@ def _extra_rotation_ablation(w, k, v, stream, steps, pf_out):
 
     # ---- ALiBi (score-space positional method, no rotation) on the position-free pool
     db = prepare(w, k, v, pos_encoding="alibi", max_pos=rows)
-    _, ams, _, _ = time_launches(lambda: db.run(stream), steps, 3, stream)
+    _, ams, _, _ = time_launches(lambda: db.run(stream), steps, 3, stream, min_warm_s=WARM_S)
     res["alibi"] = {"decode_event_ms_mean": round(ams, 5),
                     "decode_gbs_logical": round(nbytes / (ams * 1e-3) / 1e9, 1)}
     return res
@@ -431,7 +451,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4],
                     help="headline workload: 2 decode (default), 3 prefill, 4 long decode")
     ap.add_argument("--no-extra", action="store_true")
@@ -471,7 +491,8 @@ def main():
     ablation = None
     if w.kind == "decode":
         log("timing headline decode")
-        main_res = run_decode_workload(w, k, v, stream, args.steps, args.warmup, args.split_blocks)
+        main_res = run_decode_workload(w, k, v, stream, args.steps, args.warmup, args.split_blocks,
+                                       min_warm_s=0.0)
         if not args.no_extra:
             log("rotation ablation: doc-local pool and materialised copies")
             try:
@@ -489,7 +510,7 @@ def main():
                             wl_name, main_res["workspace_bytes"] > 0)
     else:
         log("timing headline prefill")
-        main_res = run_prefill_workload(w, k, v, stream, args.steps, args.warmup)
+        main_res = run_prefill_workload(w, k, v, stream, args.steps, args.warmup, min_warm_s=0.0)
         ms = main_res["wall_ms_per_step"]
         value, unit = main_res["flops"] / (ms * 1e-3) / 1e12, "TFLOP/s"
         config["new_tokens_per_request"] = int(w.q_len(0))
