@@ -11,13 +11,15 @@
 // a q tile is 256 MFMA rows = (256 / G) new tokens x the G query heads of the
 // kv head, so the GQA group shares every staged K/V tile and the rotation of a
 // key is amortised over 256 query rows.  Wave w owns rows 32w .. 32w+31.
-// Per 64-key tile (4 blocks), double-buffered in LDS.  Staging runs two tiles
-// ahead and hides behind the MFMAs: while the S MFMAs of tile t execute, each
-// wave rotates and stores its keys of tile t+1 (loaded one iteration earlier)
-// into the other buffer and issues the key loads of tile t+2; while the P.V
-// MFMAs execute it does the same for the values.  Staging has no branches
-// (tiles past the end read the request's last block and are zeroed), so each
-// MFMA phase is one basic block the scheduler can interleave.
+// Per 64-key tile (4 blocks), double-buffered in LDS.  Key staging runs two
+// tiles ahead and hides behind the MFMAs: while the S MFMAs of tile t execute,
+// each wave rotates and stores its keys of tile t+1 (loaded one iteration
+// earlier) into the other buffer and issues the key loads of tile t+2.  Values
+// need no arithmetic, so they go from the pool straight into LDS
+// (global_load_lds, no registers): the loads of tile t+1 are issued at the
+// start of iteration t and waited for at its closing barrier.  Key staging has
+// no branches (tiles past the end read the request's last block and are
+// zeroed), so each MFMA phase is one basic block the scheduler can interleave.
 //   S'^T[64 keys x 32 rows]  = K' Q^T - m   18 x v_mfma_f32_32x32x16_bf16
 //   O^T[128 dims x 32 rows] += V^T P^T      16 x v_mfma_f32_32x32x16_bf16
 // The softmax reference -m of each row rides in the S product as one extra
@@ -27,8 +29,10 @@
 // cancels in O / l, and it keeps p <= 2^8.  The S accumulator gives each lane
 // one query row, so row statistics are in-lane plus one cross-half shuffle,
 // and after exp2 and bf16 rounding the accumulator registers are exactly the B
-// operand of the P.V product.  V is read dim-major from the pool and stored in
-// LDS in the key order that makes each lane's 8-key A operand one 16-byte read.
+// operand of the P.V product.  Keys sit in LDS in an order (row = key index
+// with bits 2 and 3 swapped) that makes each lane's eight P values of a P.V
+// k-step eight consecutive keys, so the matching V^T operand is one 16-byte
+// chunk of the dim-major pool, copied to LDS as is.
 // Causal masking is applied only on blocks flagged causal (the new tokens);
 // trailing causal blocks no row of the workgroup can see are skipped.
 //
@@ -66,21 +70,20 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// LDS K' tile: [64 keys][16 chunks of 8 dims]; chunk index XOR-swizzled by key.
-__device__ __forceinline__ int k_lds_off(int key, int chunk) {
-  return key * D + ((chunk ^ (key & 15)) << 3);
+// LDS K' tile: [64 rows][16 chunks of 8 dims]; chunk index XOR-swizzled by row.
+__device__ __forceinline__ int k_lds_off(int row, int chunk) {
+  return row * D + ((chunk ^ (row & 15)) << 3);
 }
 // LDS V^T tile: [128 dims][8 chunks of 8 keys]; chunk index XOR-swizzled by dim.
 __device__ __forceinline__ int v_lds_off(int dim, int chunk) {
   return dim * KT + ((chunk ^ ((dim >> 1) & 7)) << 3);
 }
 
-// Registers of one tile in flight between global memory and LDS.
+// Registers of one key tile in flight between global memory and LDS.
 struct Staged {
   uint4 k1, k2;      // key chunk cp and its rotation partner cp + 8
   float4 c0, c1;     // cos of pairs 8cp .. 8cp+7 at the key's position
   float4 s0, s1;     // sin of the same pairs
-  uint4 v[2];        // two 16-byte V^T chunks (unused slots zeroed)
 };
 
 // MODE: 0 RoPE over a position-free pool, 1 RoPE over a document-local pool,
@@ -106,7 +109,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
   if (qt * TQ >= nq) return;
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * KT];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[D * KT];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[D * KT];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -206,15 +210,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
   }
 
   // ---- staging roles.  Wave w stages keys 8w .. 8w+7 of a tile, which all sit in
-  // block w / 2, and V chunks of blocks w / 4 and 2 + w / 4: every pool base
-  // address is wave-uniform (scalar), lanes add 32-bit offsets.
+  // block w / 2 (a wave-uniform pool base, lanes add 32-bit offsets), and V^T
+  // dims 16w .. 16w+15.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int kk = tid >> 3;  // key of the tile
   const int cp = tid & 7;   // chunk cp (dims 8cp..) and partner cp + 8
   const int kslot = kk & 15;
   const int kblk = wave_u >> 1;
-  const int vrem = tid & 255;
-  const uint32_t v_off = static_cast<uint32_t>((vrem >> 1) * BS + 8 * (vrem & 1));
 
   auto load_k = [&](int tb, Staged& st) {
     // Branch-free: a block past the end reads the request's last block (valid
@@ -248,26 +250,56 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     }
   };
 
-  auto load_v = [&](int tb, Staged& st) {
+  // V^T of the tile starting at block tb, straight from the pool into LDS
+  // (global_load_lds, 16 B per lane: keys 8c .. 8c+7 of one dim are contiguous
+  // in the dim-major pool).  Wave w fills dims 16w .. 16w+15; lane l of a load
+  // lands at chunk slot l % 8 of dim row l / 8, which holds logical chunk
+  // (l % 8) ^ swizzle(dim).  Returns the four blocks' valid-slot counts packed
+  // 5 bits each (0 for blocks past the end, which read the last block).
+  auto dma_v = [&](int tb, uint16_t* vbuf) {
+    uint32_t ids[BPT];
+    uint32_t pack = 0;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int vb = 2 * u + (wave_u >> 2);
-      const bool blk_ok = tb + vb < rb1;
-      const BlockWord w = unpack_word(words[min(tb + vb, rb1 - 1)]);
-      const uint16_t* vbase = v_pool + (static_cast<size_t>(w.block_id) * Hkv + g) * (D * BS);
-      const uint4 x = *reinterpret_cast<const uint4*>(vbase + v_off);
-      // zero slots >= n_valid among 8half .. 8half+7 (unused slots may hold anything)
-      const int nv = blk_ok ? w.n_valid - 8 * (vrem & 1) : 0;
-      const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-      uint32_t ys[4];
+    for (int b = 0; b < BPT; ++b) {
+      const BlockWord w = unpack_word(words[min(tb + b, rb1 - 1)]);
+      ids[b] = w.block_id;
+      pack |= static_cast<uint32_t>(tb + b < rb1 ? w.n_valid : 0) << (5 * b);
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t keep = (2 * e < nv ? 0x0000FFFFu : 0u) | (2 * e + 1 < nv ? 0xFFFF0000u : 0u);
-        ys[e] = xs[e] & keep;
+    for (int i = 0; i < 2; ++i) {
+      const int dim = 16 * wave_u + 8 * i + (lane >> 3);
+      const int c = (lane & 7) ^ ((dim >> 1) & 7);
+      const int bb = c >> 1;
+      const uint32_t id = bb == 0 ? ids[0] : bb == 1 ? ids[1] : bb == 2 ? ids[2] : ids[3];
+      const uint16_t* src =
+          v_pool + (static_cast<size_t>(id) * Hkv + g) * (D * BS) + dim * BS + 8 * (c & 1);
+      __builtin_amdgcn_global_load_lds(src, vbuf + (16 * wave_u + 8 * i) * KT, 16, 0, 0);
+    }
+    return pack;
+  };
+  // Zero the V^T entries of unused slots (partial or missing blocks) of a tile
+  // whose DMA has completed: they may hold anything, and 0 * NaN is NaN.
+  auto fix_v = [&](uint32_t pack, uint16_t* vbuf) {
+    const int b = tid >> 7;
+    const int dim = tid & 127;
+    const int nv = static_cast<int>((pack >> (5 * b)) & 31u);
+    if (nv < BS) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint4* ptr = reinterpret_cast<uint4*>(&vbuf[v_lds_off(dim, 2 * b + h)]);
+        const uint4 x = *ptr;
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+        uint32_t ys[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k0 = 8 * h + 2 * e;
+          ys[e] = xs[e] & ((k0 < nv ? 0x0000FFFFu : 0u) | (k0 + 1 < nv ? 0xFFFF0000u : 0u));
+        }
+        *ptr = uint4{ys[0], ys[1], ys[2], ys[3]};
       }
-      st.v[u] = uint4{ys[0], ys[1], ys[2], ys[3]};
     }
   };
+  constexpr uint32_t FULL_PACK = 16u | (16u << 5) | (16u << 10) | (16u << 15);
 
   auto store_k = [&](const Staged& st, int buf) {
     const float cc[8] = {st.c0.x, st.c0.y, st.c0.z, st.c0.w, st.c1.x, st.c1.y, st.c1.z, st.c1.w};
@@ -291,23 +323,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
       p1[e2] = pack_bf16x2(y1[0], y1[1]);
       p2[e2] = pack_bf16x2(y2[0], y2[1]);
     }
-    *reinterpret_cast<uint4*>(&k_lds[buf][k_lds_off(kk, cp)]) = o1;
-    *reinterpret_cast<uint4*>(&k_lds[buf][k_lds_off(kk, cp + 8)]) = o2;
-  };
-
-  auto store_v = [&](const Staged& st, int buf) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int vb = 2 * u + (wave_u >> 2);
-      const int dim = vrem >> 1;
-      const int half = vrem & 1;
-      // slots 8half + [0,4) -> keys 16vb + 4half + [0,4); slots + 4 -> 16vb + 8 + 4half + [0,4)
-      const int k0 = 16 * vb + 4 * half;
-      *reinterpret_cast<uint2*>(&v_lds[buf][v_lds_off(dim, k0 >> 3) + (k0 & 7)]) =
-          uint2{st.v[u].x, st.v[u].y};
-      *reinterpret_cast<uint2*>(&v_lds[buf][v_lds_off(dim, (k0 + 8) >> 3) + (k0 & 7)]) =
-          uint2{st.v[u].z, st.v[u].w};
-    }
+    // key kk sits in LDS row kk with bits 2 and 3 swapped, so that each lane's
+    // eight P values of a P.V k-step are eight consecutive keys
+    const int krow = (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+    *reinterpret_cast<uint4*>(&k_lds[buf][k_lds_off(krow, cp)]) = o1;
+    *reinterpret_cast<uint4*>(&k_lds[buf][k_lds_off(krow, cp + 8)]) = o2;
   };
 
   float lrun = 0.f;
@@ -319,21 +339,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
 
   const int ntiles = (rb1 - rb0 + BPT - 1) / BPT;
   Staged st;
+  uint32_t pack_cur = FULL_PACK;  // valid-slot counts of the current tile
   if (ntiles > 0) {
+    pack_cur = dma_v(rb0, v_lds0);
     load_k(rb0, st);
-    load_v(rb0, st);
     store_k(st, 0);
-    store_v(st, 0);
-    if (ntiles > 1) {
-      load_k(rb0 + BPT, st);
-      load_v(rb0 + BPT, st);
-    }
+    load_k(rb0 + BPT, st);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  // One tile: V^T of this tile is in vcur (loaded during the previous
+  // iteration), the V loads of the next tile go to vdma.  The two V buffers are
+  // separate arrays and the loop is unrolled by two, so the compiler can tell
+  // the in-flight loads from the LDS reads and does not wait for them early.
+  auto run_tile = [&](int it, uint16_t* vcur, uint16_t* vdma) {
     const int tb = rb0 + it * BPT;
     const int buf = it & 1;
+    if (pack_cur != FULL_PACK) {  // rare: partial or missing blocks
+      fix_v(pack_cur, vcur);
+      __syncthreads();
+    }
+    const uint32_t pack_new = dma_v(tb + BPT, vdma);
 
     // Tile metadata (uniform): up to 4 blocks; missing blocks have no valid keys.
     int t_nv[BPT], t_pos0[BPT];
@@ -375,18 +402,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     // the other buffer, then start the loads of tile it + 2.
     store_k(st, buf ^ 1);  // past the last tile: a buffer nobody reads
     load_k(tb + 2 * BPT, st);
-    // sacc[tk][rr] = score(key 32tk + 8(rr/4) + 4h2 + rr%4, this lane's row) - mref
+    // sacc[tk][rr] = score(key 32tk + 16(rr/8) + 8h2 + 4((rr/4)%2) + rr%4, this
+    // lane's row) - mref
     if (ALIBI) {
-      // + slope * (p - m); the key of sacc[tk][rr] is slot 8((rr/4)%2) + 4h2 + rr%4 of
+      // + slope * (p - m); the key of sacc[tk][rr] is slot 8h2 + 4((rr/4)%2) + rr%4 of
       // block 2tk + rr/8
       float base[BPT];
 #pragma unroll
-      for (int b = 0; b < BPT; ++b) base[b] = slope2 * static_cast<float>(t_pos0[b] + 4 * h2 - qpos);
+      for (int b = 0; b < BPT; ++b) base[b] = slope2 * static_cast<float>(t_pos0[b] + 8 * h2 - qpos);
 #pragma unroll
       for (int tk = 0; tk < 2; ++tk)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr)
-          sacc[tk][rr] += __builtin_fmaf(slope2, static_cast<float>(8 * ((rr >> 2) & 1) + (rr & 3)),
+          sacc[tk][rr] += __builtin_fmaf(slope2, static_cast<float>(4 * ((rr >> 2) & 1) + (rr & 3)),
                                          base[2 * tk + (rr >> 3)]);
     }
     if (!tile_simple) {
@@ -398,12 +426,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
       for (int bb = 0; bb < BPT; ++bb)
         lim[bb] = t_causal[bb] ? min(t_nv[bb], qpos - t_pos0[bb] + 1) : t_nv[bb];
       asm volatile("" : "+v"(lim[0]), "+v"(lim[1]), "+v"(lim[2]), "+v"(lim[3]));
-      // key 32tk + 8(rr/4) + 4h2 + rr%4 lies in block 2tk + rr/8, slot 8((rr/4)%2) + 4h2 + rr%4
+      // the key of sacc[tk][rr] lies in block 2tk + rr/8, slot 8h2 + 4((rr/4)%2) + rr%4
 #pragma unroll
       for (int tk = 0; tk < 2; ++tk)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-          const int sl = 8 * ((rr >> 2) & 1) + 4 * h2 + (rr & 3);
+          const int sl = 8 * h2 + 4 * ((rr >> 2) & 1) + (rr & 3);
           sacc[tk][rr] = sl < lim[2 * tk + (rr >> 3)] ? sacc[tk][rr] : -INFINITY;
         }
     }
@@ -456,6 +484,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
       pb[u] = as_bf16x8(pk);
     }
     lrun += psum;
+    pack_cur = pack_new;
 
     __builtin_amdgcn_iglp_opt(1);
     // ---- O^T += V^T P^T
@@ -465,13 +494,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const uint4 a =
-            *reinterpret_cast<const uint4*>(&v_lds[buf][v_lds_off(32 * t + col, 2 * u + h2)]);
+            *reinterpret_cast<const uint4*>(&vcur[v_lds_off(32 * t + col, 2 * u + h2)]);
         oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[u], oacc[t], 0, 0, 0);
       }
-    // While the P.V MFMAs run: V of tile it + 1, then the V loads of tile it + 2.
-    store_v(st, buf ^ 1);
-    load_v(tb + 2 * BPT, st);
+    // The V loads of the next tile (and the key loads) land before the barrier.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    run_tile(it, v_lds0, v_lds1);
+    if (it + 1 < ntiles) run_tile(it + 1, v_lds1, v_lds0);
   }
 
   // ---- epilogue: O / l -> bf16; lse
