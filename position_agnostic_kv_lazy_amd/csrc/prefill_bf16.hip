@@ -70,6 +70,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+// The value lane l ^ 32 holds, paired with this lane's own: gfx950's
+// v_permlane32_swap exchanges the two 32-lane halves in registers (no LDS
+// round trip, unlike a shuffle).  The two results are {own, other} in some
+// order on every lane, so a symmetric combine of them needs no lane select.
+struct HalfPair {
+  float a, b;
+};
+__device__ __forceinline__ HalfPair half_swap(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 // LDS K' tile: [64 rows][16 chunks of 8 dims]; chunk index XOR-swizzled by row.
 __device__ __forceinline__ int k_lds_off(int row, int chunk) {
   return row * D + ((chunk ^ (row & 15)) << 3);
@@ -255,13 +267,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
   // in the dim-major pool).  Wave w fills dims 16w .. 16w+15; lane l of a load
   // lands at chunk slot l % 8 of dim row l / 8, which holds logical chunk
   // (l % 8) ^ swizzle(dim).  Returns the four blocks' valid-slot counts packed
-  // 5 bits each (0 for blocks past the end, which read the last block).
-  auto dma_v = [&](int tb, uint16_t* vbuf) {
+  // 5 bits each (0 for blocks past the end, which read the last block), and
+  // leaves the four (clamped) words in wout for the iteration that reads the
+  // tile, which then needs no scalar loads of its own.
+  auto dma_v = [&](int tb, uint16_t* vbuf, uint64_t (&wout)[BPT]) {
     uint32_t ids[BPT];
     uint32_t pack = 0;
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
-      const BlockWord w = unpack_word(words[min(tb + b, rb1 - 1)]);
+      wout[b] = words[min(tb + b, rb1 - 1)];
+      const BlockWord w = unpack_word(wout[b]);
       ids[b] = w.block_id;
       pack |= static_cast<uint32_t>(tb + b < rb1 ? w.n_valid : 0) << (5 * b);
     }
@@ -340,8 +355,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
   const int ntiles = (rb1 - rb0 + BPT - 1) / BPT;
   Staged st;
   uint32_t pack_cur = FULL_PACK;  // valid-slot counts of the current tile
+  uint64_t wcur[BPT] = {0, 0, 0, 0};  // its block words (clamped to the last block)
   if (ntiles > 0) {
-    pack_cur = dma_v(rb0, v_lds0);
+    pack_cur = dma_v(rb0, v_lds0, wcur);
     load_k(rb0, st);
     store_k(st, 0);
     load_k(rb0 + BPT, st);
@@ -360,25 +376,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
       fix_v(pack_cur, vcur);
       __syncthreads();
     }
-    const uint32_t pack_new = dma_v(tb + BPT, vdma);
+    uint64_t wnew[BPT];
+    const uint32_t pack_new = dma_v(tb + BPT, vdma, wnew);
 
-    // Tile metadata (uniform): up to 4 blocks; missing blocks have no valid keys.
+    // Tile metadata (uniform), from the words the previous iteration loaded with
+    // this tile's values: re-loading them here cost a chain of scalar loads, each
+    // waited for, before the first MFMA of every tile.  A missing block has no
+    // valid keys (its word is the request's last block's).
     int t_nv[BPT], t_pos0[BPT];
     bool t_causal[BPT];
-    bool tile_simple = true;
+    bool tile_simple = pack_cur == FULL_PACK;
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
-      if (tb + b < rb1) {
-        const BlockWord w = unpack_word(words[tb + b]);
-        t_nv[b] = w.n_valid;
-        t_pos0[b] = w.pos0;
-        t_causal[b] = w.causal;
-      } else {
-        t_nv[b] = 0;
-        t_pos0[b] = 0;
-        t_causal[b] = false;
-      }
-      tile_simple = tile_simple && t_nv[b] == BS && !t_causal[b];
+      const BlockWord w = unpack_word(wcur[b]);
+      t_nv[b] = static_cast<int>((pack_cur >> (5 * b)) & 31u);
+      t_pos0[b] = w.pos0;
+      t_causal[b] = w.causal;
+      tile_simple = tile_simple && !t_causal[b];
     }
 
     // Both MFMA phases ask the scheduler for its MFMA / LDS-read interleave
@@ -443,7 +457,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
       for (int rr = 0; rr < 16; rr += 2)
         tmax = __builtin_elementwise_maximum(
             tmax, __builtin_elementwise_maximum(sacc[tk][rr], sacc[tk][rr + 1]));
-    tmax = __builtin_elementwise_maximum(tmax, __shfl_xor(tmax, 32, 64));
+    {
+      const HalfPair hp = half_swap(tmax);
+      tmax = __builtin_elementwise_maximum(hp.a, hp.b);
+    }
     const bool raise = (tmax > RESCALE_THRESHOLD) || (!mset && tmax != -INFINITY);
     float delta = 0.f;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -485,6 +502,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     }
     lrun += psum;
     pack_cur = pack_new;
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) wcur[b] = wnew[b];
 
     __builtin_amdgcn_iglp_opt(1);
     // ---- O^T += V^T P^T
@@ -507,7 +526,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
   }
 
   // ---- epilogue: O / l -> bf16; lse
-  lrun += __shfl_xor(lrun, 32, 64);
+  {
+    const HalfPair hp = half_swap(lrun);
+    lrun = hp.a + hp.b;
+  }
   if (!row_valid) return;
   const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;
   uint16_t* orow = out + (static_cast<size_t>(q_begin + jt) * Hq + head) * D;
