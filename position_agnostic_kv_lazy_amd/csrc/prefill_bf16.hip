@@ -18,8 +18,9 @@
 // need no arithmetic, so they go from the pool straight into LDS
 // (global_load_lds, no registers): the loads of tile t+1 are issued at the
 // start of iteration t and waited for at its closing barrier.  Key staging has
-// no branches (tiles past the end read the request's last block and are
-// zeroed), so each MFMA phase is one basic block the scheduler can interleave.
+// no branches (a tile past the end reads the request's last block, an unused
+// slot its block's last key: real, finite keys whose scores the mask removes),
+// so each MFMA phase is one basic block the scheduler can interleave.
 //   S'^T[64 keys x 32 rows]  = K' Q^T - m   18 x v_mfma_f32_32x32x16_bf16
 //   O^T[128 dims x 32 rows] += V^T P^T      16 x v_mfma_f32_32x32x16_bf16
 // The softmax reference -m of each row rides in the S product as one extra
@@ -232,8 +233,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
 
   auto load_k = [&](int tb, Staged& st) {
     // Branch-free: a block past the end reads the request's last block (valid
-    // memory) and is zeroed; unused slots are zeroed too.
-    const bool blk_ok = tb + kblk < rb1;
+    // memory) and an unused slot its block's last key.  Neither is zeroed: a key
+    // row of K' only reaches its own scores, and every tile holding such keys
+    // (pack != FULL_PACK) takes the masked path, which sets those scores to -inf.
     const BlockWord w = unpack_word(words[min(tb + kblk, rb1 - 1)]);
     const uint16_t* kb = k_pool + (static_cast<size_t>(w.block_id) * Hkv + g) * (BS * D);
     const float* row;
@@ -242,16 +244,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     } else if (DOC_LOCAL) {
       row = cs + static_cast<size_t>(w.causal ? p0 : w.pos0) * D + 8 * cp;
     } else {
-      // unused slots keep K = 0 and read the table row of the block's last key
+      // unused slots read the table row of the block's last key
       row = cs + static_cast<size_t>(w.pos0) * D +
             static_cast<uint32_t>(min(kslot, w.n_valid - 1) * D + 8 * cp);
     }
     const uint32_t off = static_cast<uint32_t>(min(kslot, w.n_valid - 1) * D + 8 * cp);
     const uint4 k1 = *reinterpret_cast<const uint4*>(kb + off);
     const uint4 k2 = *reinterpret_cast<const uint4*>(kb + off + HALF);
-    const bool keep = blk_ok && kslot < w.n_valid;
-    st.k1 = keep ? k1 : uint4{0u, 0u, 0u, 0u};
-    st.k2 = keep ? k2 : uint4{0u, 0u, 0u, 0u};
+    st.k1 = k1;
+    st.k2 = k2;
     if (!ALIBI) {
       st.c0 = *reinterpret_cast<const float4*>(row);
       st.c1 = *reinterpret_cast<const float4*>(row + 4);
@@ -449,14 +450,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
           sacc[tk][rr] = sl < lim[2 * tk + (rr >> 3)] ? sacc[tk][rr] : -INFINITY;
         }
     }
-    // NaN-propagating max (v_maximum3_f32): no canonicalisation of MFMA results
-    float tmax = -INFINITY;
+    // NaN-propagating max (v_maximum3_f32): no canonicalisation of MFMA results.
+    // One chain of three-input maxima: 16 instructions for the 32 scores.
+    float tmax = __builtin_elementwise_maximum(sacc[0][0], sacc[0][1]);
 #pragma unroll
-    for (int tk = 0; tk < 2; ++tk)
-#pragma unroll
-      for (int rr = 0; rr < 16; rr += 2)
-        tmax = __builtin_elementwise_maximum(
-            tmax, __builtin_elementwise_maximum(sacc[tk][rr], sacc[tk][rr + 1]));
+    for (int i = 2; i < 32; i += 2)
+      tmax = __builtin_elementwise_maximum(
+          __builtin_elementwise_maximum(tmax, sacc[i >> 4][i & 15]), sacc[i >> 4][(i & 15) + 1]);
     {
       const HalfPair hp = half_swap(tmax);
       tmax = __builtin_elementwise_maximum(hp.a, hp.b);
