@@ -87,10 +87,19 @@ __device__ __forceinline__ HalfPair half_swap(float x) {
 __device__ __forceinline__ int k_lds_off(int row, int chunk) {
   return row * D + ((chunk ^ (row & 15)) << 3);
 }
-// LDS V^T tile: [128 dims][8 chunks of 8 keys]; chunk index XOR-swizzled by dim.
-__device__ __forceinline__ int v_lds_off(int dim, int chunk) {
-  return dim * KT + ((chunk ^ ((dim >> 1) & 7)) << 3);
+// LDS V^T tile: one 4 KB sub-tile per block, [4 segments of 32 dims] x
+// [64 16-byte chunks]; a chunk holds keys 8c .. 8c+7 (c = 0, 1) of one dim.
+// Chunk (dim d of the segment, c) sits in 128-byte row (d & 1) | (d >> 4) << 1
+// | c << 2 at 16-byte column c ^ ((d >> 1) & 7): the eight rows of a segment
+// give each (column, row) pair one chunk, and the 32 lanes that read one c of
+// 32 consecutive dims see the same bank pattern as an XOR-swizzled [dim][keys]
+// tile (conflict-free).  Element offset of the chunk inside its segment:
+__device__ __forceinline__ int v_seg_off(int d, int c) {
+  const int row = (d & 1) | ((d >> 4) << 1) | (c << 2);
+  return (row * 8 + (c ^ ((d >> 1) & 7))) * 8;
 }
+constexpr int V_SEG = 32 * 16;      // elements per 32-dim segment
+constexpr int V_BLK = 4 * V_SEG;    // elements per block sub-tile
 
 // Registers of one key tile in flight between global memory and LDS.
 struct Staged {
@@ -230,6 +239,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
   const int cp = tid & 7;   // chunk cp (dims 8cp..) and partner cp + 8
   const int kslot = kk & 15;
   const int kblk = wave_u >> 1;
+  // P.V operand of this lane: dim col of a segment, key chunk h2
+  const int v_rd = v_seg_off(col, h2);
 
   auto load_k = [&](int tb, Staged& st) {
     // Branch-free: a block past the end reads the request's last block (valid
@@ -265,31 +276,35 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
 
   // V^T of the tile starting at block tb, straight from the pool into LDS
   // (global_load_lds, 16 B per lane: keys 8c .. 8c+7 of one dim are contiguous
-  // in the dim-major pool).  Wave w fills dims 16w .. 16w+15; lane l of a load
-  // lands at chunk slot l % 8 of dim row l / 8, which holds logical chunk
-  // (l % 8) ^ swizzle(dim).  Returns the four blocks' valid-slot counts packed
-  // 5 bits each (0 for blocks past the end, which read the last block), and
-  // leaves the four (clamped) words in wout for the iteration that reads the
-  // tile, which then needs no scalar loads of its own.
+  // in the dim-major pool).  Wave w fills segments 2(w & 1), 2(w & 1) + 1 of
+  // block w / 2, one load each, so a load reads one pool block (a wave-uniform
+  // base): lane l lands at chunk l of the segment and fetches the (dim, c) that
+  // v_seg_off places there, a lane constant.  Returns the four blocks'
+  // valid-slot counts packed 5 bits each (0 for blocks past the end, which read
+  // the last block), and leaves the four (clamped) words in wout for the
+  // iteration that reads the tile, which then needs no scalar loads of its own.
+  const uint32_t v_lane_off = [&] {
+    const int row = lane >> 3, col8 = lane & 7;
+    const int c = row >> 2;
+    const int d = (row & 1) | (((col8 ^ c) & 7) << 1) | (((row >> 1) & 1) << 4);
+    return static_cast<uint32_t>(d * BS + 8 * c);
+  }();
   auto dma_v = [&](int tb, uint16_t* vbuf, uint64_t (&wout)[BPT]) {
-    uint32_t ids[BPT];
     uint32_t pack = 0;
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
       wout[b] = words[min(tb + b, rb1 - 1)];
       const BlockWord w = unpack_word(wout[b]);
-      ids[b] = w.block_id;
       pack |= static_cast<uint32_t>(tb + b < rb1 ? w.n_valid : 0) << (5 * b);
     }
+    // (this wave's block word again: a scalar-cache hit, and no branches)
+    const uint32_t vid = unpack_word(words[min(tb + kblk, rb1 - 1)]).block_id;
+    const uint16_t* vb = v_pool + (static_cast<size_t>(vid) * Hkv + g) * (D * BS);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int dim = 16 * wave_u + 8 * i + (lane >> 3);
-      const int c = (lane & 7) ^ ((dim >> 1) & 7);
-      const int bb = c >> 1;
-      const uint32_t id = bb == 0 ? ids[0] : bb == 1 ? ids[1] : bb == 2 ? ids[2] : ids[3];
-      const uint16_t* src =
-          v_pool + (static_cast<size_t>(id) * Hkv + g) * (D * BS) + dim * BS + 8 * (c & 1);
-      __builtin_amdgcn_global_load_lds(src, vbuf + (16 * wave_u + 8 * i) * KT, 16, 0, 0);
+      const int seg = 2 * (wave_u & 1) + i;
+      __builtin_amdgcn_global_load_lds(vb + seg * V_SEG + v_lane_off,
+                                       vbuf + kblk * V_BLK + seg * V_SEG, 16, 0, 0);
     }
     return pack;
   };
@@ -302,7 +317,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
     if (nv < BS) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        uint4* ptr = reinterpret_cast<uint4*>(&vbuf[v_lds_off(dim, 2 * b + h)]);
+        uint4* ptr = reinterpret_cast<uint4*>(
+            &vbuf[b * V_BLK + (dim >> 5) * V_SEG + v_seg_off(dim & 31, h)]);
         const uint4 x = *ptr;
         const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
         uint32_t ys[4];
@@ -513,7 +529,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const uint4 a =
-            *reinterpret_cast<const uint4*>(&vcur[v_lds_off(32 * t + col, 2 * u + h2)]);
+            *reinterpret_cast<const uint4*>(&vcur[u * V_BLK + t * V_SEG + v_rd]);
         oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[u], oacc[t], 0, 0, 0);
       }
     // The V loads of the next tile (and the key loads) land before the barrier.
