@@ -51,6 +51,21 @@ constexpr int D = 128;
 constexpr int HALF = 64;
 constexpr int BS = 16;
 constexpr int WAVES = 4;
+
+// Max (or sum) of x over lanes l and l ^ 16, and over l and l ^ 32, with
+// gfx950's v_permlane16_swap / v_permlane32_swap: the lane exchange happens in
+// registers (a shuffle goes through LDS).  Each swap returns {own, partner} in
+// some order on every lane, and max and sum are symmetric.
+__device__ __forceinline__ float xor16_combine(float x, bool take_max) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return take_max ? fmaxf(a, b) : a + b;
+}
+__device__ __forceinline__ float xor32_combine(float x, bool take_max) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return take_max ? fmaxf(a, b) : a + b;
+}
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -138,8 +153,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
 #pragma unroll
   for (int j = 0; j < 8; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Block words are loaded one block ahead: loading a block's word at the top
+  // of its own iteration put a full memory round trip in front of its K/V loads.
+  uint64_t w_next = gb0 + wave < gb1 ? words[gb0 + wave] : 0;
   for (int b = gb0 + wave; b < gb1; b += WAVES) {
-    const BlockWord w = unpack_word(words[b]);
+    const BlockWord w = unpack_word(w_next);
+    w_next = words[min(b + WAVES, gb1 - 1)];  // past the end: a valid word, unused
     const size_t tile = static_cast<size_t>(w.block_id) * Hkv + g;
     // Issue the K and V loads first (4 x 16 B and 8 x 8 B per lane).
     const uint16_t* kb = k_pool + tile * (BS * D) + n * D;
@@ -249,8 +268,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
         if (4 * gq + i >= w.n_valid) sacc[i] = -INFINITY;
     }
     float bm = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    bm = xor16_combine(bm, true);
+    bm = xor32_combine(bm, true);
     const float mnew = fmaxf(mrun, bm);
     const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
     float p[4];
@@ -282,8 +301,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
   }
 
   // Wave state -> LDS: lane (n, gq) holds O^T[16j + 4gq + i][head n].
-  lrun += __shfl_xor(lrun, 16, 64);
-  lrun += __shfl_xor(lrun, 32, 64);
+  lrun = xor16_combine(lrun, false);
+  lrun = xor32_combine(lrun, false);
   if (n < G) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
