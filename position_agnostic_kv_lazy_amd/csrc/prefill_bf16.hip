@@ -28,7 +28,7 @@
 // subtraction.  The reference is only raised when a row's max exceeds it by
 // more than 2^8 (then O and l are rescaled); any reference is exact because it
 // cancels in O / l, and it keeps p <= 2^8.  The S accumulator gives each lane
-// one query row, so row statistics are in-lane plus one cross-half shuffle,
+// one query row, so row statistics are in-lane plus one half-wave exchange,
 // and after exp2 and bf16 rounding the accumulator registers are exactly the B
 // operand of the P.V product.  Keys sit in LDS in an order (row = key index
 // with bits 2 and 3 swapped) that makes each lane's eight P values of a P.V
