@@ -64,7 +64,8 @@ def traffic_for(kind, workload):
 
 
 def time_launches(run, steps, warmup, stream, flush=None, min_warm_s=0.0):
-    """Warm up, then time exactly `steps` launches: wall clock and per-launch HIP events.
+    """Warm up, then time exactly `steps` back-to-back launches by wall clock, and
+    `steps` more with per-launch HIP events.
 
     The GPU raises its clocks only after some tens of milliseconds of sustained
     work (a 0.17 ms decode launch runs about 10 % slower for its first ~150
@@ -81,9 +82,19 @@ def time_launches(run, steps, warmup, stream, flush=None, min_warm_s=0.0):
         if done % 50 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    # Wall clock: exactly `steps` launches back to back, with nothing else on
+    # the stream (per-launch event records would add their own gaps).
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if flush is not None:
+            flush()
+        run()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # Per-launch durations: the same `steps` launches again, each bracketed by
+    # HIP events on the launch stream.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
-    t0 = time.perf_counter()
     for a, b in evs:
         if flush is not None:
             flush()
@@ -91,7 +102,6 @@ def time_launches(run, steps, warmup, stream, flush=None, min_warm_s=0.0):
         run()
         b.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = [a.elapsed_time(b) for a, b in evs]  # ms
     return wall, float(np.mean(per)), float(np.median(per)), per
 
