@@ -44,7 +44,12 @@
  *           for the other stored forms)
  *  v_pool   [num_blocks][num_kv_heads][head_dim][block_size]   V, dim-major
  *           inside each (block, kv head) tile, so the token axis -- the
- *           contraction axis of P.V -- is contiguous.
+ *           contraction axis of P.V -- is contiguous.  Why: the MFMA A operand
+ *           of the P.V product is 4 (decode) or 8 (prefill) consecutive keys
+ *           of one dimension, which this layout makes one 8- or 16-byte load
+ *           (and lets prefill copy V tiles to LDS unchanged); a token-major
+ *           tile would need a transpose per operand.  lazy_attn_store_kv
+ *           writes this layout from token-major [token][kv head][dim] input.
  *  cos_sin  float32 [max_pos][2][head_dim/2]: row p holds cos(p theta_i) then
  *           sin(p theta_i).  Build it with lazy_attn_rope_table or
  *           lazy_attn_rope_table_scaled (float64 arithmetic, rounded once to
@@ -117,6 +122,11 @@ typedef enum la_dtype { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
  *    0's logical position (the causal mask needs it) and are rotated by
  *    q_pos0.  Decode tables must not flag blocks causal in this mode.  A pool
  *    pre-rotated at absolute positions is the special case s = 0.
+ *    Tables whose rows carry an amplitude a (cos and sin both times a, as
+ *    lazy_attn_rope_table_scaled writes for YaRN) give every score a^2 in
+ *    every mode: stored keys written with such a table carry a once, decode
+ *    rotates q with the table (a), and prefill divides its relative key
+ *    rotation by a, read as row 0's first cosine (a * cos 0).
  */
 typedef enum la_pool_mode { LA_POOL_POSITION_FREE = 0, LA_POOL_DOC_LOCAL = 1 } la_pool_mode;
 
@@ -190,7 +200,10 @@ LA_API la_status lazy_attn_rope_table(double base, int32_t head_dim, int32_t row
  *  LA_SCALING_YARN    per pair, theta_i for pairs that turn more than
  *                     beta_fast times over original_max_pos, theta_i / factor
  *                     for pairs that turn less than beta_slow times, a linear
- *                     ramp over the pair index in between; cos and sin are
+ *                     ramp over the pair index in between (ramp ends: the
+ *                     fractional pair indices of beta_fast rounded down and of
+ *                     beta_slow rounded up, clamped to [0, head_dim - 1] as in
+ *                     the published correction range); cos and sin are
  *                     multiplied by attn_factor (0 = 0.1 ln(factor) + 1)
  *  LA_SCALING_LLAMA3  wavelength 2 pi / theta_i below original_max_pos /
  *                     high_freq_factor kept, above original_max_pos /
@@ -260,9 +273,16 @@ LA_API la_status lazy_attn_pack_segments(const la_params* p, int32_t batch, cons
 /*
  * Check a packed table against the pool and position limits (debug helper).
  * Arrays may be host or device memory (device ones are copied synchronously).
+ *   blk_words      rows 0 .. req_blk_start[batch]-1 are read; row b is
+ *                  blk_words[b] (the absolute index the kernels use, also when
+ *                  req_blk_start[0] > 0)
  *   q_pos   decode: query position per request; prefill: position of the
  *           first new token per request
  *   cu_q    prefill: [batch+1] query row offsets; NULL for decode
+ *   max_blocks_per_req  the value that will be passed to lazy_attn_decode
+ *           (0 = not checked): a request with more blocks fails validation
+ *   max_q_per_req       the value that will be passed to lazy_attn_prefill
+ *           (0 = not checked): a request with more query rows fails
  * Decode requires every key position < max_pos and q_pos < max_pos; prefill
  * requires q_pos + (cu_q[r+1]-cu_q[r]) - 1 < max_pos and that each new-token
  * row sees at least one key.  With LA_POOL_DOC_LOCAL, decode tables may not
@@ -271,7 +291,8 @@ LA_API la_status lazy_attn_pack_segments(const la_params* p, int32_t batch, cons
  */
 LA_API la_status lazy_attn_validate_table(const la_params* p, int32_t batch, const uint64_t* blk_words,
                                    const int32_t* req_blk_start, const int32_t* q_pos,
-                                   const int32_t* cu_q);
+                                   const int32_t* cu_q, int32_t max_blocks_per_req,
+                                   int32_t max_q_per_req);
 
 /*
  * Bytes of device workspace lazy_attn_decode needs for this shape (0 when the
@@ -313,7 +334,11 @@ LA_API la_status lazy_attn_store_kv(const la_params* p, const void* k, const voi
  *   q_pos          device [batch] logical position m of each query
  *   cos_sin        device [max_pos][2][D/2] float32 (LA_ALIBI: the slopes,
  *                  float32 [num_q_heads])
- *   max_blocks_per_req  host scalar: upper bound of per-request block counts
+ *   max_blocks_per_req  host scalar: upper bound of per-request block counts.
+ *                  The grid (split groups x blocks per group) is sized from
+ *                  it, so a request with more blocks has its trailing blocks
+ *                  silently ignored (a wrong result with LA_OK); pass it to
+ *                  lazy_attn_validate_table to have that checked
  *   out            device [batch][Hq][D] (same dtype as q)
  *   lse            device [batch][Hq] float32 or NULL
  *   workspace      device, >= lazy_attn_decode_workspace_size bytes (may be
@@ -336,7 +361,9 @@ LA_API la_status lazy_attn_decode(const la_params* p, const void* q, const void*
  *   q          device [total_q][Hq][D]; cu_q device [batch+1]
  *   q_pos0     device [batch]: logical position of request r's first new
  *              token; new token j sits at q_pos0[r] + j
- *   max_q_per_req  host scalar: upper bound of cu_q[r+1] - cu_q[r]
+ *   max_q_per_req  host scalar: upper bound of cu_q[r+1] - cu_q[r].  The
+ *              grid's q tiles are sized from it: rows of a longer request
+ *              beyond it are never written (lazy_attn_validate_table checks)
  *   out        device [total_q][Hq][D]; lse device [total_q][Hq] or NULL
  * The new tokens' own K/V must already be in the pool, in blocks flagged
  * causal.  Every query row must see at least one key.  bf16 mode needs

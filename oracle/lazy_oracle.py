@@ -109,8 +109,9 @@ def rope_theta_scaled(head_dim: int, base: float, scaling=None):
       yarn:   per pair, wavelength-dependent blend of theta_i (fast pairs) and
               theta_i / s (slow pairs) over a linear ramp between the pair
               indices where the rotation count over the original context is
-              beta_fast and beta_slow; cos and sin scaled by the attention
-              factor (default 0.1 ln s + 1);
+              beta_fast (rounded down) and beta_slow (rounded up, clamped to
+              D - 1 as in the published correction range); cos and sin scaled
+              by the attention factor (default 0.1 ln s + 1);
       llama3: wavelength 2 pi / theta_i below L/high_freq_factor kept, above
               L/low_freq_factor divided by s, smooth blend in between.
     scaling: None or a dict with "type" and the parameters above
@@ -121,7 +122,9 @@ def rope_theta_scaled(head_dim: int, base: float, scaling=None):
     linear scaling maps positions (s m, s n) to the plain scores at (m, n);
     NTK keeps the fastest pair and divides the slowest by s; YaRN and llama3
     keep fast pairs, divide slow pairs by s and are monotone between; YaRN's
-    amplitude at s = e is 1.1.
+    amplitude at s = e is 1.1; the exact ramp ends lo = 40, hi = 65 and the
+    resulting frequencies at D = 128, base 1e4, original context 65536, where
+    the D - 1 clamp matters (hi > D/2 - 1).
     """
     theta = rope_theta(head_dim, base)
     if scaling is None or scaling.get("type", "none") == "none":
@@ -140,8 +143,12 @@ def rope_theta_scaled(head_dim: int, base: float, scaling=None):
         def pair_index(rotations):  # pair whose rotations over L equal `rotations`
             return D * np.log(L / (rotations * 2.0 * np.pi)) / (2.0 * np.log(base))
 
+        # The published correction range: floor / ceil of the two fractional
+        # pair indices, clamped to [0, D - 1] (an upper bound above the last
+        # pair index D/2 - 1: when it binds, the ramp over the D/2 pairs stops
+        # short of 1 and the slowest pairs are only partly interpolated).
         lo = max(np.floor(pair_index(bf)), 0.0)
-        hi = min(np.ceil(pair_index(bs)), D / 2 - 1.0)
+        hi = min(np.ceil(pair_index(bs)), D - 1.0)
         if lo == hi:
             hi += 0.001
         ramp = np.clip((np.arange(D // 2) - lo) / (hi - lo), 0.0, 1.0)
@@ -212,15 +219,19 @@ def _segment_starts(segments) -> np.ndarray:
 def _encode_keys(K, pos, segments, theta, doc_local, pairing="half", amp=1.0):
     """Keys encoded at their logical positions.
 
-    Position-free pool: R_p k.  Document-local pool (stored R_t k): R_s of the
-    stored key, s = the segment's start, which is R_{s+t} k.
+    Position-free pool: R_p k (with the table's amplitude amp).
+    Document-local pool (stored amp R_t k, written with the same table): the
+    pure rotation by s = the segment's start of the stored key, which is
+    amp R_{s+t} k -- the amplitude is already in the stored key, so a scaled
+    table's attention factor is applied once per key either way.
     """
     if doc_local:
-        return rope_rotate(K, _segment_starts(segments), theta, pairing, amp)
+        return rope_rotate(K, _segment_starts(segments), theta, pairing)
     return rope_rotate(K, pos, theta, pairing, amp)
 
 
-def store_kv(k, v, slots, rope_pos, k_pool, v_pool, *, block_size, theta, pairing="half"):
+def store_kv(k, v, slots, rope_pos, k_pool, v_pool, *, block_size, theta, pairing="half",
+             amp=1.0):
     """The cache write: new tokens' keys and values into pool slots.
 
     Token n goes to block slots[n] // BS, slot slots[n] % BS; its key is
@@ -231,7 +242,8 @@ def store_kv(k, v, slots, rope_pos, k_pool, v_pool, *, block_size, theta, pairin
     slots not listed keep their old contents.  With interleaved pairing the
     key is rotated on pairs (2i, 2i+1) and then stored with its dimensions in
     the order (even dims, odd dims) -- the storage order of such pools, which
-    turns each pair back into (i, i + D/2).
+    turns each pair back into (i, i + D/2).  amp is the amplitude of a scaled
+    table's rows (its cos and sin both carry it), applied with the rotation.
 
     Pins: rope_pos None is an exact copy; a rotated key equals the complex
     product x * exp(j p theta) and keeps its norm; Example 3.1 through
@@ -243,7 +255,7 @@ def store_kv(k, v, slots, rope_pos, k_pool, v_pool, *, block_size, theta, pairin
     slots = np.asarray(slots, np.int64)
     blk, sl = slots // block_size, slots % block_size
     if rope_pos is not None:
-        kf = rope_rotate(kf, np.asarray(rope_pos, np.int64)[:, None], theta, pairing)
+        kf = rope_rotate(kf, np.asarray(rope_pos, np.int64)[:, None], theta, pairing, amp)
     if pairing == "interleaved":
         kf = np.concatenate([kf[..., 0::2], kf[..., 1::2]], axis=-1)
     kp[blk, :, sl, :] = kf

@@ -134,7 +134,8 @@ _lib.lazy_attn_pack_segments.restype = ctypes.c_int
 _lib.lazy_attn_pack_segments.argtypes = [_prm, ctypes.c_int32, _i64p, _i64p, _i64p, _u8p, _i64p,
                                          _i64p, _u64p, ctypes.c_int64, _i32p, _i32p]
 _lib.lazy_attn_validate_table.restype = ctypes.c_int
-_lib.lazy_attn_validate_table.argtypes = [_prm, ctypes.c_int32, _P, _P, _P, _P]
+_lib.lazy_attn_validate_table.argtypes = [_prm, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32,
+                                          ctypes.c_int32]
 _lib.lazy_attn_decode_workspace_size.restype = ctypes.c_int
 _lib.lazy_attn_decode_workspace_size.argtypes = [_prm, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.POINTER(ctypes.c_size_t)]
@@ -278,9 +279,10 @@ def _hptr(x):
 
 
 def lazy_attn_validate_table(params: la_params, batch: int, blk_words, req_blk_start, q_pos,
-                             cu_q=None):
+                             cu_q=None, max_blocks_per_req: int = 0, max_q_per_req: int = 0):
     _check(_lib.lazy_attn_validate_table(ctypes.byref(params), batch, _hptr(blk_words),
-                                         _hptr(req_blk_start), _hptr(q_pos), _hptr(cu_q)),
+                                         _hptr(req_blk_start), _hptr(q_pos), _hptr(cu_q),
+                                         int(max_blocks_per_req), int(max_q_per_req)),
            "lazy_attn_validate_table")
 
 

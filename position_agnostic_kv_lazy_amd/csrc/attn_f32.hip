@@ -10,7 +10,9 @@
 // Document-local pools (keys stored as R_t k with t the index inside the
 // segment): decode rotates q by m - s per block (s = the segment start the word
 // carries) and uses the keys as stored; prefill rotates each key by s once
-// (for the causal blocks s is the request's first new position).  ALiBi: no
+// (for the causal blocks s is the request's first new position), as a pure
+// rotation: stored keys already carry a scaled table's amplitude, which row
+// 0's first cosine gives, so the rotated query is divided by it.  ALiBi: no
 // rotation; each score gets slope_h * (p - m).  Interleaved RoPE: lane i loads
 // q elements (2i, 2i+1); keys of such pools are stored (even, odd) dims.
 #include "device_common.hpp"
@@ -64,6 +66,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
       const float s = cs[static_cast<size_t>(qp) * D + HALF + i];
       q1 = x1 * c - x2 * s;
       q2 = x1 * s + x2 * c;
+      if (DOC_LOCAL) {  // doc-local prefill: pure relative key rotation
+        q1 /= cs[0];
+        q2 /= cs[0];
+      }
     }
   }
 

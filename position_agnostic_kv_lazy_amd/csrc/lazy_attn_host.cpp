@@ -217,8 +217,10 @@ LA_API la_status lazy_attn_rope_table_scaled(double base, int32_t head_dim, int3
         auto index_of = [&](double turns) {
           return D * std::log(L / (turns * 2.0 * M_PI)) / (2.0 * std::log(base));
         };
+        // correction range as published: clamped to [0, D - 1], which can lie
+        // past the last pair (then the slowest pairs are only partly scaled)
         const double lo = std::max(std::floor(index_of(bf)), 0.0);
-        double hi = std::min(std::ceil(index_of(bs)), static_cast<double>(half - 1));
+        double hi = std::min(std::ceil(index_of(bs)), D - 1.0);
         if (hi == lo) hi += 0.001;
         for (int i = 0; i < half; ++i) {
           const double w = std::min(std::max((i - lo) / (hi - lo), 0.0), 1.0);  // 1 = interpolate
@@ -367,7 +369,8 @@ LA_API la_status lazy_attn_pack_segments(const la_params* p, int32_t batch,
 
 LA_API la_status lazy_attn_validate_table(const la_params* p, int32_t batch,
                                           const uint64_t* blk_words, const int32_t* req_blk_start,
-                                          const int32_t* q_pos, const int32_t* cu_q) {
+                                          const int32_t* q_pos, const int32_t* cu_q,
+                                          int32_t max_blocks_per_req, int32_t max_q_per_req) {
   try {
     la_status st = check_params(p);
     if (st != LA_OK) return st;
@@ -378,9 +381,23 @@ LA_API la_status lazy_attn_validate_table(const la_params* p, int32_t batch,
     if ((st = fetch(req_blk_start, batch + 1, rbs)) != LA_OK) return st;
     if ((st = fetch(q_pos, batch, qp)) != LA_OK) return st;
     if (cu_q && (st = fetch(cu_q, batch + 1, cq)) != LA_OK) return st;
+    if (max_blocks_per_req < 0 || max_q_per_req < 0)
+      return fail(LA_ERR_INVALID_ARG, "max_blocks_per_req / max_q_per_req must be >= 0");
     if (rbs[0] < 0) return fail(LA_ERR_INVALID_ARG, "req_blk_start[0] < 0");
-    for (int r = 0; r < batch; ++r)
+    for (int r = 0; r < batch; ++r) {
       if (rbs[r + 1] <= rbs[r]) return fail(LA_ERR_INVALID_ARG, "request %d has no blocks", r);
+      // the launch sizes its grid from these bounds: rows beyond them are never read
+      if (max_blocks_per_req > 0 && rbs[r + 1] - rbs[r] > max_blocks_per_req)
+        return fail(LA_ERR_INVALID_ARG, "request %d has %d blocks > max_blocks_per_req %d", r,
+                    rbs[r + 1] - rbs[r], max_blocks_per_req);
+      if (cu_q && max_q_per_req > 0 &&
+          static_cast<int64_t>(cq[r + 1]) - cq[r] > max_q_per_req)
+        return fail(LA_ERR_INVALID_ARG, "request %d has %lld query rows > max_q_per_req %d", r,
+                    static_cast<long long>(cq[r + 1]) - cq[r], max_q_per_req);
+    }
+    // The kernels index blk_words with the absolute row numbers of
+    // req_blk_start, so rows [0, req_blk_start[batch]) are fetched and row b
+    // is words[b].
     std::vector<uint64_t> words;
     if ((st = fetch(blk_words, static_cast<size_t>(rbs[batch]), words)) != LA_OK) return st;
     for (int r = 0; r < batch; ++r) {
@@ -393,7 +410,7 @@ LA_API la_status lazy_attn_validate_table(const la_params* p, int32_t batch,
       int64_t min_causal = INT64_MAX;
       bool has_cached = false;
       for (int32_t b = rbs[r]; b < rbs[r + 1]; ++b) {
-        const uint64_t wd = words[b - rbs[0]];
+        const uint64_t wd = words[b];
         const int64_t id = static_cast<int64_t>(wd & 0xFFFFFFFFull);
         const int64_t pos0 = static_cast<int64_t>((wd >> 32) & 0xFFFFFFull);
         const int nv = static_cast<int>((wd >> 56) & 0x7Full) + 1;

@@ -41,7 +41,11 @@
 // every key of a block is rotated by the same offset s, the segment start its
 // word carries (for causal blocks, whose words keep slot 0's position for the
 // mask, s is the request's first new position), so one table row serves a
-// whole document -- the single relative rotation of §3.2 "Prefilling".
+// whole document -- the single relative rotation of §3.2 "Prefilling".  A
+// stored key already carries the amplitude of a scaled table (YaRN's
+// attention factor on cos and sin), so the relative rotation must be a pure
+// one: the 1 / amplitude it needs (row 0's first cosine is the amplitude) is
+// folded into the query scale, since every key of such a pool takes it.
 //
 // ALiBi (§3.5): neither q nor keys are rotated; each score gets
 // slope_h * (p - m) in fp32 after the S product.  Interleaved RoPE pairs
@@ -140,6 +144,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_bf16_kernel(
   const int col = lane & 31;  // MFMA column: this lane's query row within the wave
   const int h2 = lane >> 5;   // MFMA k-half
   const int p0 = q_pos0[r];
+  if (DOC_LOCAL) qscale /= cs[0];  // pure relative key rotation (see above)
 
   // ---- this lane's query row: rotate to its position, scale, round to bf16
   const int rho = wave * 32 + col;

@@ -100,14 +100,15 @@ def params_for(w, num_blocks: int, max_pos: Optional[int] = None, split_blocks: 
 def store_pool(w, k_tok: np.ndarray, v_tok: np.ndarray, slots: np.ndarray,
                rope_pos: Optional[np.ndarray], device="cuda", num_blocks: Optional[int] = None,
                max_pos: Optional[int] = None, fill: float = 0.0, stream=None,
-               pos_encoding="rope_half"):
+               pos_encoding="rope_half", table: Optional[np.ndarray] = None):
     """Build a device pool pair by writing tokens with lazy_attn_store_kv.
 
     k_tok / v_tok: host [n, Hkv, D] in the pool encoding; slots: flat slot ids;
     rope_pos: per-token rotation position or None (keys stored as given).
     pos_encoding="rope_interleaved" rotates pairs (2i, 2i+1) and stores keys in
-    (even dims, odd dims) order.  Unlisted slots hold `fill`.  Returns
-    (k_dev, v_dev) in the device layouts.
+    (even dims, odd dims) order.  table overrides the cos/sin rows used for
+    the rotation (e.g. a scaled RoPE table).  Unlisted slots hold `fill`.
+    Returns (k_dev, v_dev) in the device layouts.
     """
     nb = int(num_blocks) if num_blocks is not None else int(w.num_blocks)
     rows = int(max_pos) if max_pos is not None else int(w.table_rows())
@@ -139,7 +140,9 @@ def store_pool(w, k_tok: np.ndarray, v_tok: np.ndarray, slots: np.ndarray,
     rp = None if rope_pos is None else torch.from_numpy(np.asarray(rope_pos, np.int32)).to(device)
     cs = None
     if rope_pos is not None:
-        cs = torch.from_numpy(B.lazy_attn_rope_table(w.rope_base, D, rows)).to(device)
+        if table is None:
+            table = B.lazy_attn_rope_table(w.rope_base, D, rows)
+        cs = torch.from_numpy(np.ascontiguousarray(table, np.float32)).to(device)
     B.lazy_attn_store_kv(params, k, v, len(slots), sl, rp, cs, k_dev, v_dev, stream)
     return k_dev, v_dev
 

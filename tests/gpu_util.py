@@ -76,7 +76,8 @@ class Device:
         if validate:
             cu = None if w.kind == "decode" else np.asarray(w.cu_q, np.int32)
             lazy_attn_validate_table(db.params, db.batch, db.host_words, db.host_rbs,
-                                     np.asarray(w.q_pos, np.int32), cu)
+                                     np.asarray(w.q_pos, np.int32), cu, db.max_blocks,
+                                     db.max_q if cu is not None else 0)
         db.run()
         torch.cuda.synchronize()
         return db.out_f32(), db.lse.cpu().numpy(), db

@@ -183,6 +183,52 @@ def test_validate_table_host_arrays():
         la.lazy_attn_validate_table(p_small, w.batch, words, rbs, qpos)
 
 
+def test_validate_table_reads_absolute_rows():
+    """Rows are blk_words[b] for b in [req_blk_start[0], req_blk_start[batch]), the
+    indices the kernels use, also when the first request does not start at row 0
+    (a sub-batch slice of one CSR table)."""
+    p = _params(num_blocks=10, max_pos=100)
+    segs = [[Segment(0, 16, np.array([1]), False)],
+            [Segment(0, 32, np.array([2, 3]), False)],
+            [Segment(0, 16, np.array([4]), False)]]
+    words, rbs, _ = la.lazy_attn_pack_segments(p, segs)
+    qpos = np.array([40, 40, 40], np.int32)
+    la.lazy_attn_validate_table(p, 3, words, rbs, qpos)
+    # requests 1 and 2 alone, rows 1 .. 3 of the same table
+    sub = rbs[1:].copy()
+    la.lazy_attn_validate_table(p, 2, words, sub, qpos[1:])
+    # a bad block id in the slice's last row must be caught ...
+    bad = words.copy()
+    bad[3] = (bad[3] & ~np.uint64(0xFFFFFFFF)) | np.uint64(12)
+    with pytest.raises(la.LazyAttnError, match="block id 12"):
+        la.lazy_attn_validate_table(p, 2, bad, sub, qpos[1:])
+    # ... and so must a bad position there
+    bad = words.copy()
+    bad[3] = (bad[3] & ~(np.uint64(0xFFFFFF) << np.uint64(32))) | (np.uint64(95) << np.uint64(32))
+    with pytest.raises(la.LazyAttnError, match="position 110"):
+        la.lazy_attn_validate_table(p, 2, bad, sub, qpos[1:])
+
+
+def test_validate_table_checks_launch_bounds():
+    """Requests longer than the max_blocks_per_req / max_q_per_req a launch is sized
+    from would be cut short silently: the validator rejects them."""
+    p = _params(num_blocks=10, max_pos=200)
+    segs = [[Segment(0, 16, np.array([1]), False)],
+            [Segment(0, 40, np.array([2, 3, 4]), False)]]
+    words, rbs, maxb = la.lazy_attn_pack_segments(p, segs)
+    assert maxb == 3
+    qpos = np.array([60, 60], np.int32)
+    la.lazy_attn_validate_table(p, 2, words, rbs, qpos, None, 3)
+    with pytest.raises(la.LazyAttnError, match="max_blocks_per_req 2"):
+        la.lazy_attn_validate_table(p, 2, words, rbs, qpos, None, 2)
+    with pytest.raises(la.LazyAttnError, match="must be >= 0"):
+        la.lazy_attn_validate_table(p, 2, words, rbs, qpos, None, -1)
+    cu = np.array([0, 5, 25], np.int32)
+    la.lazy_attn_validate_table(p, 2, words, rbs, qpos, cu, 3, 20)
+    with pytest.raises(la.LazyAttnError, match="max_q_per_req 19"):
+        la.lazy_attn_validate_table(p, 2, words, rbs, qpos, cu, 3, 19)
+
+
 def test_validate_table_prefill_needs_visible_key():
     p = _params(num_blocks=10, max_pos=100)
     segs = [[Segment(50, 5, np.array([1]), True)]]
@@ -288,6 +334,8 @@ def test_pos_encoding_checks():
     {"type": "yarn", "factor": 16.0, "original_max_pos": 4096, "beta_fast": 32.0, "beta_slow": 1.0},
     {"type": "yarn", "factor": 4.0, "original_max_pos": 8192, "beta_fast": 32.0, "beta_slow": 1.0,
      "attn_factor": 1.3},
+    {"type": "yarn", "factor": 16.0, "original_max_pos": 65536, "beta_fast": 32.0,
+     "beta_slow": 1.0},
     {"type": "llama3", "factor": 8.0, "original_max_pos": 8192, "low_freq_factor": 1.0,
      "high_freq_factor": 4.0},
 ], ids=lambda d: d["type"])

@@ -164,6 +164,42 @@ def test_doc_local_prefill(dtype):
         assert_parity(out[a:b], ref_pf[r][0], dtype, f"doc-local vs position-free req {r}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_doc_local_with_scaled_table(kind, dtype):
+    """A YaRN table carries an amplitude on cos and sin (its attention factor).
+    Keys written by lazy_attn_store_kv with that table carry it once; decode
+    (q rotated with the table) and prefill (relative key rotation made pure)
+    must then both give amp^2 on every score, like the position-free path
+    (§3.5: scaled variants change only the table)."""
+    from oracle import rope_theta_scaled
+    from position_agnostic_kv_lazy_amd import lazy_attn_rope_table_scaled
+    sc = {"type": "yarn", "factor": 16.0, "original_max_pos": 256, "beta_fast": 32.0,
+          "beta_slow": 1.0}
+    w = _tiny(kind, dtype)
+    rows = int(w.table_rows())
+    table = lazy_attn_rope_table_scaled(w.rope_base, w.head_dim, rows, sc)
+    k, v, slots, idx = segment_writes(w, "index")
+    log(f"doc-local {kind} {dtype} with a YaRN table (amplitude {float(table[0, 0]):.4f})")
+    kd, vd = store_pool(w, k, v, slots, idx, table=table)
+    torch.cuda.synchronize()
+    out, lse, _ = Device.from_device_pools(kd, vd).run(w, pool_mode="doc_local", table=table)
+    th, amp = rope_theta_scaled(w.head_dim, w.rope_base, sc)
+    base = np.zeros(w.k_pool.shape)
+    pools = store_kv(k, v, slots, idx, base, base, block_size=w.block_size, theta=th, amp=amp)
+    run = run_decode if kind == "decode" else run_prefill
+    ref = run(w, pools=pools, doc_local=True, scaling=sc)
+    ref_pf = run(w, scaling=sc)
+    for r in range(w.batch):
+        sl = slice(r, r + 1) if kind == "decode" else slice(int(w.cu_q[r]), int(w.cu_q[r + 1]))
+        o, l = out[sl], lse[sl]
+        want, want_l = ref[r][0].reshape(o.shape), ref[r][1].reshape(l.shape)
+        assert_parity(o, want, dtype, f"doc-local yarn {kind} req {r}")
+        assert_lse(l, want_l, dtype, f"doc-local yarn {kind} req {r}")
+        assert_parity(o, ref_pf[r][0].reshape(o.shape), dtype,
+                      f"doc-local yarn {kind} vs position-free req {r}")
+
+
 def test_absolute_prerotated_pool_decode():
     """Keys pre-rotated at absolute positions, every word's start 0 (rotation-off baseline)."""
     reqs = [[("doc", 0), ("doc", 2), ("priv", 3)], [("doc", 1, 30), ("doc", 3, 200)]]

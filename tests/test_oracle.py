@@ -734,6 +734,95 @@ def test_yarn_ramp_follows_rotation_counts_and_attention_factor():
     assert abs(amp_e - 1.1) < 1e-15
 
 
+def test_yarn_ramp_ends_where_the_upper_clamp_binds():
+    """YaRN's correction range, hand-computed for D = 128, base 1e4, original
+    context L = 65536, beta_fast 32, beta_slow 1 (the published definition the
+    table restates; LazyAttention §3.5 only says scaled variants change the
+    table).  The pair index turning b times over L is
+    D ln(L / (2 pi b)) / (2 ln base): 40.21 for b = 32 and 64.29 for b = 1, so
+    the ramp runs from lo = floor(40.21) = 40 to hi = ceil(64.29) = 65.  hi lies
+    past the last pair (63): the published range clamps it to D - 1 = 127,
+    not to 63, so pair 63 is only 23/25 interpolated.  A floor/ceil swap at
+    either end, or a D/2 - 1 clamp, changes pair 41 or pair 63 below.
+    """
+    from oracle import rope_theta_scaled
+    D, base, L, f = 128, 1e4, 65536, 16.0
+    th, amp = rope_theta_scaled(D, base, {"type": "yarn", "factor": f, "original_max_pos": L,
+                                          "beta_fast": 32.0, "beta_slow": 1.0})
+    th0 = 1.0 / (1e4 ** (np.arange(0, D, 2, dtype=np.float64) / D))  # textbook frequencies
+    lo, hi = 40, 65  # literal, from the arithmetic in the docstring
+    for i, ramp in [(0, 0.0), (39, 0.0), (40, 0.0), (41, 1 / 25), (52, 12 / 25), (63, 23 / 25)]:
+        want = th0[i] * (1.0 - ramp) + th0[i] / f * ramp
+        assert abs(th[i] - want) <= 1e-15 * th0[i], (i, th[i], want)
+        assert ramp == max(0.0, min(1.0, (i - lo) / (hi - lo)))
+    assert abs(amp - (0.1 * math.log(16.0) + 1.0)) < 1e-15
+
+
+def test_scaled_amplitude_enters_every_score_squared_in_both_pool_readings():
+    """A table whose rows carry an amplitude a (cos and sin both times a) scales
+    every score by a^2 -- once through the query, once through the key -- in the
+    position-free reading and in the document-local one, where the stored key
+    (written with the table) already carries a and the relative rotation by the
+    segment start is a pure rotation.  Pinned to the scalar brute force with
+    scale * a^2 (LazyAttention §3.5: a scaled variant keeps q^T R_{n-m} k)."""
+    from oracle import store_kv
+    from oracle.brute import brute_attention
+    a = 1.37
+    for kind in ("decode", "prefill"):
+        w = _tiny(kind, dtype="f32")
+        th = rope_theta(w.head_dim, w.rope_base)
+        slots, idx, ks, vs = [], [], [], []
+        seen = set()
+        for segs in w.requests:
+            for seg in segs:
+                key = tuple(int(b) for b in seg.blocks)
+                if key in seen:
+                    continue
+                seen.add(key)
+                t = np.arange(seg.n_tokens)
+                blk = np.asarray(seg.blocks)[t // w.block_size]
+                slots.append(blk * w.block_size + t % w.block_size)
+                idx.append(t)
+                ks.append(w.k_pool[blk, :, t % w.block_size, :])
+                vs.append(w.v_pool[blk, :, t % w.block_size, :])
+        slots, idx = np.concatenate(slots), np.concatenate(idx)
+        base_pool = np.zeros(w.k_pool.shape)
+        pools = store_kv(np.concatenate(ks), np.concatenate(vs), slots, idx, base_pool, base_pool,
+                         block_size=w.block_size, theta=th, amp=a)
+        kw = dict(block_size=w.block_size, num_kv_heads=w.num_kv_heads, theta=th, scale=w.scale,
+                  amp=a)
+        G = w.num_q_heads // w.num_kv_heads
+        for r, segs in enumerate(w.requests):
+            if kind == "decode":
+                o_pf, _ = attention_decode(w.q[r], int(w.q_pos[r]), segs, w.k_pool, w.v_pool, **kw)
+                o_dl, _ = attention_decode(w.q[r], int(w.q_pos[r]), segs, *pools, doc_local=True,
+                                           **kw)
+                qrows = [(w.q[r][h], int(w.q_pos[r]), h) for h in range(w.num_q_heads)]
+            else:
+                qa, qb = int(w.cu_q[r]), int(w.cu_q[r + 1])
+                o_pf, _ = attention_prefill(w.q[qa:qb], int(w.q_pos[r]), segs, w.k_pool, w.v_pool,
+                                            **kw)
+                o_dl, _ = attention_prefill(w.q[qa:qb], int(w.q_pos[r]), segs, *pools,
+                                            doc_local=True, **kw)
+                qrows = [(w.q[qa + j][h], int(w.q_pos[r]) + j, (j, h))
+                         for j in range(qb - qa) for h in range(w.num_q_heads)]
+            for qv, qp, at in qrows:
+                h = at if kind == "decode" else at[1]
+                g = h // G
+                keys = []
+                for seg in segs:
+                    for t in range(seg.n_tokens):
+                        b, sl = int(seg.blocks[t // w.block_size]), t % w.block_size
+                        keys.append((w.k_pool[b, g, sl].tolist(), w.v_pool[b, g, sl].tolist(),
+                                     int(seg.start) + t, bool(seg.is_new)))
+                (want, _), = brute_attention([(qv.tolist(), qp)], keys, w.scale * a * a,
+                                             w.rope_base)
+                got_pf = o_pf[h] if kind == "decode" else o_pf[at]
+                got_dl = o_dl[h] if kind == "decode" else o_dl[at]
+                np.testing.assert_allclose(got_pf, want, rtol=0, atol=1e-12)
+                np.testing.assert_allclose(got_dl, want, rtol=0, atol=1e-12)
+
+
 def test_llama3_scaling_wavelength_classes():
     from oracle import rope_theta_scaled
     D, base, L = 128, 5e5, 8192
