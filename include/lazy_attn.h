@@ -355,6 +355,31 @@ LA_API la_status lazy_attn_decode(const la_params* p, const void* q, const void*
                            void* stream);
 
 /*
+ * Allocation-free decode, for callers that cannot allocate device memory or
+ * hand the library a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, semantics and
+ * kernels as lazy_attn_decode without the workspace pair: the split-group
+ * partials live in a fixed device array inside the library,
+ * LA_DECODE_NOALLOC_SCRATCH_BYTES per GPU (one copy on each GPU the library
+ * runs on, held until the process ends; its address is resolved on the first
+ * call on each device).  Shapes whose partials would exceed it (those for
+ * which lazy_attn_decode_workspace_size returns more) are rejected with
+ * LA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  The call allocates
+ * nothing.  Every call on one GPU shares that GPU's array; each launch writes
+ * every partial it later reads, so nothing needs clearing between calls, but
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * on it and must be serialised by the caller.
+ */
+#define LA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+LA_API la_status lazy_attn_decode_noalloc(const la_params* p, const void* q, const void* k_pool,
+                                          const void* v_pool, const uint64_t* blk_words,
+                                          const int32_t* req_blk_start, const int32_t* q_pos,
+                                          const float* cos_sin, int32_t batch,
+                                          int32_t max_blocks_per_req, void* out, float* lse,
+                                          void* stream);
+
+/*
  * Prefill: the new prompt tokens of each request attend every cached key of
  * the request and, among the new tokens, causally (§3.2 "Prefilling"; §3.4
  * Eq. 7 TTFT model: attention of the L' new tokens against all L keys).

@@ -29,6 +29,7 @@ from .binding import (  # noqa: F401
     lazy_attn_decode_workspace_size,
     lazy_attn_store_kv,
     lazy_attn_decode,
+    lazy_attn_decode_noalloc,
     lazy_attn_prefill,
     lazy_attn_cache_simulate,
 )

@@ -32,6 +32,7 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE_TOO_SMALL, LA_ERR_HIP = range(5)
+LA_DECODE_NOALLOC_SCRATCH_BYTES = 8 << 20  # the header's fixed decode scratch per GPU
 LA_BF16, LA_FP32 = 0, 1
 LA_POOL_POSITION_FREE, LA_POOL_DOC_LOCAL = 0, 1
 LA_ROPE_HALF, LA_ROPE_INTERLEAVED, LA_ALIBI = 0, 1, 2
@@ -49,6 +50,7 @@ EXPORTED = (
     "lazy_attn_decode_workspace_size",
     "lazy_attn_store_kv",
     "lazy_attn_decode",
+    "lazy_attn_decode_noalloc",
     "lazy_attn_prefill",
     "lazy_attn_cache_simulate",
 )
@@ -144,6 +146,9 @@ _lib.lazy_attn_store_kv.argtypes = [_prm, _P, _P, ctypes.c_int64, _P, _P, _P, _P
 _lib.lazy_attn_decode.restype = ctypes.c_int
 _lib.lazy_attn_decode.argtypes = [_prm, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                   _P, _P, _P, ctypes.c_size_t, _P]
+_lib.lazy_attn_decode_noalloc.restype = ctypes.c_int
+_lib.lazy_attn_decode_noalloc.argtypes = [_prm, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                          ctypes.c_int32, _P, _P, _P]
 _lib.lazy_attn_cache_simulate.restype = ctypes.c_int
 _lib.lazy_attn_cache_simulate.argtypes = [ctypes.c_int64, _i64p, _i32p, ctypes.c_int32,
                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _i64p]
@@ -308,6 +313,16 @@ def lazy_attn_decode(params: la_params, q, k_pool, v_pool, blk_words, req_blk_st
                                  _ptr(blk_words), _ptr(req_blk_start), _ptr(q_pos), _ptr(cos_sin),
                                  batch, max_blocks_per_req, _ptr(out), _ptr(lse), _ptr(workspace),
                                  ws_bytes, _stream(stream)), "lazy_attn_decode")
+
+
+def lazy_attn_decode_noalloc(params: la_params, q, k_pool, v_pool, blk_words, req_blk_start,
+                             q_pos, cos_sin, batch: int, max_blocks_per_req: int, out, lse=None,
+                             stream=None):
+    _check(_lib.lazy_attn_decode_noalloc(ctypes.byref(params), _ptr(q), _ptr(k_pool),
+                                         _ptr(v_pool), _ptr(blk_words), _ptr(req_blk_start),
+                                         _ptr(q_pos), _ptr(cos_sin), batch, max_blocks_per_req,
+                                         _ptr(out), _ptr(lse), _stream(stream)),
+           "lazy_attn_decode_noalloc")
 
 
 def lazy_attn_prefill(params: la_params, q, k_pool, v_pool, blk_words, req_blk_start, cu_q,

@@ -39,13 +39,28 @@
 // registers.  Interleaved RoPE pairs (2i, 2i+1) only change which q elements a
 // lane loads: such pools store keys in (even dims, odd dims) order, which makes
 // every pair (i, i + D/2) again.
+#include <atomic>
 #include <climits>
+#include <mutex>
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "lazy_attn.h"
 
 namespace lazyattn {
 namespace {
+
+// Fixed scratch of the allocation-free decode entry point: the split-group
+// partials (o, m, l) that lazy_attn_decode keeps in the caller's workspace.
+// Every GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` names a host-side stand-in, never the device
+// memory: host code uses only the address hipGetSymbolAddress returns for the
+// current device (decode_scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[LA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
 
 constexpr int D = 128;
 constexpr int HALF = 64;
@@ -429,6 +444,27 @@ DecodeSplit choose_decode_split(int batch, int num_kv_heads, int max_blocks_per_
 size_t decode_workspace_bytes(int batch, int num_q_heads, int head_dim, const DecodeSplit& s) {
   if (s.groups <= 1) return 0;
   return static_cast<size_t>(batch) * num_q_heads * s.groups * (head_dim + 2) * sizeof(float);
+}
+
+hipError_t decode_scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // once per device, with that device current: this device's copy of the array
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 hipError_t launch_decode_bf16(const AttnArgs& a, const DecodeSplit& s, void* workspace,

@@ -50,6 +50,10 @@ hipError_t launch_attn_f32(const AttnArgs& a, bool prefill, hipStream_t stream);
 hipError_t launch_decode_bf16(const AttnArgs& a, const DecodeSplit& s, void* workspace,
                               hipStream_t stream);
 
+// Device address of this library's fixed decode scratch on the current device
+// (LA_DECODE_NOALLOC_SCRATCH_BYTES bytes, resolved once per device).
+hipError_t decode_scratch_ptr(void** out);
+
 // bf16 MFMA prefill.
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
 

@@ -532,6 +532,51 @@ LA_API la_status lazy_attn_decode(const la_params* p, const void* q, const void*
   }
 }
 
+LA_API la_status lazy_attn_decode_noalloc(const la_params* p, const void* q, const void* k_pool,
+                                          const void* v_pool, const uint64_t* blk_words,
+                                          const int32_t* req_blk_start, const int32_t* q_pos,
+                                          const float* cos_sin, int32_t batch,
+                                          int32_t max_blocks_per_req, void* out, float* lse,
+                                          void* stream) {
+  try {
+    la_status st = check_params(p);
+    if (st != LA_OK) return st;
+    if (!q || !k_pool || !v_pool || !blk_words || !req_blk_start || !q_pos || !cos_sin || !out)
+      return fail(LA_ERR_INVALID_ARG, "NULL device pointer passed to lazy_attn_decode_noalloc");
+    if (batch < 1 || max_blocks_per_req < 1)
+      return fail(LA_ERR_INVALID_ARG, "batch and max_blocks_per_req must be >= 1");
+    const lazyattn::AttnArgs a = make_args(p, q, k_pool, v_pool, blk_words, req_blk_start, nullptr,
+                                           q_pos, cos_sin, batch, 1, max_blocks_per_req, out, lse);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p->dtype == LA_FP32) {  // no scratch in fp32 mode
+      clear_stale_hip_error();
+      const hipError_t e = lazyattn::launch_attn_f32(a, false, s);
+      if (e != hipSuccess) return hip_fail(e, "lazy_attn_decode_noalloc launch");
+      return ok();
+    }
+    const lazyattn::DecodeSplit sp = lazyattn::choose_decode_split(
+        batch, p->num_kv_heads, max_blocks_per_req, p->split_blocks, p->target_workgroups);
+    const size_t need = lazyattn::decode_workspace_bytes(batch, p->num_q_heads, p->head_dim, sp);
+    if (need > LA_DECODE_NOALLOC_SCRATCH_BYTES)
+      return fail(LA_ERR_WORKSPACE_TOO_SMALL,
+                  "decode needs %zu scratch bytes for this shape; the fixed scratch of "
+                  "lazy_attn_decode_noalloc holds %zu (use lazy_attn_decode with a workspace, "
+                  "or a larger split_blocks)",
+                  need, static_cast<size_t>(LA_DECODE_NOALLOC_SCRATCH_BYTES));
+    void* ws = nullptr;
+    if (need > 0) {
+      const hipError_t e = lazyattn::decode_scratch_ptr(&ws);
+      if (e != hipSuccess) return hip_fail(e, "lazy_attn_decode_noalloc scratch address");
+    }
+    clear_stale_hip_error();
+    const hipError_t e = lazyattn::launch_decode_bf16(a, sp, ws, s);
+    if (e != hipSuccess) return hip_fail(e, "lazy_attn_decode_noalloc launch");
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_HIP, "unexpected exception in lazy_attn_decode_noalloc");
+  }
+}
+
 LA_API la_status lazy_attn_prefill(const la_params* p, const void* q, const void* k_pool,
                                    const void* v_pool, const uint64_t* blk_words,
                                    const int32_t* req_blk_start, const int32_t* cu_q,

@@ -25,7 +25,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -245,6 +245,22 @@ def test_null_pointers_rejected_before_launch():
         la.lazy_attn_decode(p, None, None, None, None, None, None, None, 1, 1, None)
     with pytest.raises(la.LazyAttnError, match="NULL"):
         la.lazy_attn_prefill(p, None, None, None, None, None, None, None, None, 1, 1, None)
+
+
+def test_noalloc_decode_rejects_shapes_beyond_its_scratch_before_launch():
+    """The allocation-free decode holds its partials in a fixed array: a shape
+    whose partials exceed it fails with a clear message, before any HIP call."""
+    txt = open(HEADER).read()
+    m = re.search(r"#define LA_DECODE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", txt)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.LA_DECODE_NOALLOC_SCRATCH_BYTES
+    p = _params(split_blocks=8)  # 64 x 8 pairs, 4096 blocks: 512 groups per pair
+    need = la.lazy_attn_decode_workspace_size(p, 64, 4096)
+    assert need > B.LA_DECODE_NOALLOC_SCRATCH_BYTES
+    fake = 1 << 40  # never dereferenced: the size check fails first
+    with pytest.raises(la.LazyAttnError, match="WORKSPACE_TOO_SMALL.*fixed scratch"):
+        la.lazy_attn_decode_noalloc(p, fake, fake, fake, fake, fake, fake, fake, 64, 4096, fake)
+    with pytest.raises(la.LazyAttnError, match="NULL"):
+        la.lazy_attn_decode_noalloc(p, None, None, None, None, None, None, None, 1, 1, None)
 
 
 def test_workspace_too_small_rejected_before_launch():
