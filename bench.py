@@ -1,21 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the lazy-RoPE paged attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--no-extra] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--legs L]
+                    [--no-extra] [--no-cpu]
 
 A step is one call of the hot path on one batch with every input already in
 HBM: by default the Llama-3-8B-shaped decode layer (64 requests, 10 Zipf(1.0)
 documents of 512 tokens + a 64-token question each, 32 q / 8 kv heads,
 head_dim 128, bf16).  `value` is the logical K+V bytes the step must read
 (4096 B per key across the 8 kv heads) divided by the step time, in GB/s.
-The same run also measures (unless --no-extra) the prefill, long-context
-decode and mixed decode+prefill workloads, each against its roofline, and
-(unless --no-cpu) the fp64 CPU oracle on a bounded sample of the headline
-workload.  Prints ONE JSON line.
 
-W defaults to 500 untimed launches: this GPU reaches its steady clocks only
-after some tens of milliseconds of back-to-back work, and a decode launch
-takes 0.16 ms, so a 10-launch warm-up would time the ramp.
+`roofline` is the HBM roofline of the decode kernel on the bytes HBM actually
+delivers per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE, recorded in
+profiles/traffic.json for the kernel source it was measured on) divided by
+the launch time from HIP events: shared documents are served from L2 and the
+Infinity Cache, so the logical bytes overstate what HBM moves.  The same run
+also measures (unless --no-extra) the prefill, long-context decode, mixed
+decode+prefill and no-sharing control workloads, each against its roofline,
+and (unless --no-cpu) the fp64 CPU oracle over the host cores on the whole
+headline batch and on sampled prefill rows -- whose results also check the
+outputs of the timed launches.  Prints ONE JSON line.
+
+Warm-up: every leg, the headline included, runs at least W launches and at
+least WARM_S seconds of launches before timing (this GPU reaches its steady
+clocks only after some tens of milliseconds of back-to-back work); the
+launches actually run are reported per leg.
 """
 from __future__ import annotations
 
@@ -32,14 +41,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "decode attn KV GB/s (% HBM peak) + prefill TFLOPS (% MFMA peak), 1 GPU"
-HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
-WARM_S = 0.25               # minimum warm-up (seconds of launches) for the extra workloads
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+WARM_S = 0.25                # minimum warm-up (seconds of launches) for every leg
+BF16_MAX_ABS, BF16_REL_L2 = 2e-2, 5e-3
 KERNEL_SRC = {
     "decode": os.path.join(ROOT, "position_agnostic_kv_lazy_amd", "csrc", "decode_bf16.hip"),
     "prefill": os.path.join(ROOT, "position_agnostic_kv_lazy_amd", "csrc", "prefill_bf16.hip"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+LEGS = ("headline", "ablation", "prefill", "long_decode", "mixed", "no_sharing", "references")
 
 
 def log(msg):
@@ -63,120 +74,58 @@ def traffic_for(kind, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_launches(run, steps, warmup, stream, flush=None, min_warm_s=0.0):
-    """Warm up, then time exactly `steps` back-to-back launches by wall clock, and
-    `steps` more with per-launch HIP events.
-
-    The GPU raises its clocks only after some tens of milliseconds of sustained
-    work (a 0.17 ms decode launch runs about 10 % slower for its first ~150
-    back-to-back launches), so steady-state figures need enough warm-up:
-    `warmup` launches, continued until at least `min_warm_s` seconds of them
-    have run.
-    """
-    import torch
-    t_warm = time.perf_counter()
-    done = 0
-    while done < warmup or time.perf_counter() - t_warm < min_warm_s:
-        run()
-        done += 1
-        if done % 50 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    # Wall clock: exactly `steps` launches back to back, with nothing else on
-    # the stream (per-launch event records would add their own gaps).
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        if flush is not None:
-            flush()
-        run()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # Per-launch durations: the same `steps` launches again, each bracketed by
-    # HIP events on the launch stream.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for a, b in evs:
-        if flush is not None:
-            flush()
-        a.record(stream)
-        run()
-        b.record(stream)
-    torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in evs]  # ms
-    return wall, float(np.mean(per)), float(np.median(per)), per
+# ----------------------------------------------------------------- CPU oracle
+# The oracle runs in worker processes forked before this process touches the
+# GPU; the workloads they read are module globals set before the fork.  No
+# worker ever makes a GPU call.
+_ORACLE_W = {}
 
 
-def make_flusher(nbytes=1 << 30):
-    """Overwrite a buffer larger than L2 + Infinity Cache (1 GiB) to evict the pool."""
-    import torch
-    buf = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
-
-    def flush():
-        buf.fill_(1.0)
-    return flush
+def _oracle_worker_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)  # one BLAS thread per worker process
 
 
-def run_decode_workload(w, k, v, stream, steps, warmup, split_blocks=0, min_warm_s=WARM_S):
-    from position_agnostic_kv_lazy_amd.prepare import prepare
-    db = prepare(w, k, v, split_blocks=split_blocks)
-    run = lambda: db.run(stream)  # noqa: E731
-    wall, ev_mean, ev_med, per = time_launches(run, steps, warmup, stream, min_warm_s=min_warm_s)
-    # right after the warm timing: the clocks are up, one warm-up launch suffices
-    _, cold_mean, cold_med, _ = time_launches(run, max(5, steps // 2), 1, stream, make_flusher())
-    nbytes = w.logical_kv_bytes()
-    return {
-        "logical_kv_bytes": nbytes,
-        "wall_ms_per_step": 1e3 * wall / steps,
-        "event_ms_mean": ev_mean,
-        "event_ms_median": ev_med,
-        "event_ms_p10": float(np.percentile(per, 10)),
-        "event_ms_p90": float(np.percentile(per, 90)),
-        "gbs_logical": nbytes / (ev_mean * 1e-3) / 1e9,
-        "cold_event_ms_mean": cold_mean,
-        "cold_gbs_logical": nbytes / (cold_mean * 1e-3) / 1e9,
-        "workspace_bytes": 0 if db.workspace is None else int(db.workspace.numel()),
-        "_db": db,
-    }
+def _oracle_decode_one(args):
+    key, r = args
+    from oracle import run_decode
+    out, lse = run_decode(_ORACLE_W[key], requests=[r])[r]
+    return r, out, lse
 
 
-def run_prefill_workload(w, k, v, stream, steps, warmup, min_warm_s=WARM_S):
-    from position_agnostic_kv_lazy_amd.prepare import prepare
-    db = prepare(w, k, v)
-    run = lambda: db.run(stream)  # noqa: E731
-    wall, ev_mean, ev_med, per = time_launches(run, steps, warmup, stream, min_warm_s=min_warm_s)
-    flops = w.prefill_flops()
-    return {
-        "flops": flops,
-        "wall_ms_per_step": 1e3 * wall / steps,
-        "event_ms_mean": ev_mean,
-        "event_ms_median": ev_med,
-        "event_ms_p10": float(np.percentile(per, 10)),
-        "event_ms_p90": float(np.percentile(per, 90)),
-        "tflops": flops / (ev_mean * 1e-3) / 1e12,
-        "_db": db,
-    }
+def _oracle_prefill_rows(args):
+    key, r, rows = args
+    from oracle import run_prefill
+    out, lse = run_prefill(_ORACLE_W[key], requests=[r], rows={r: np.asarray(rows)})[r]
+    return r, rows, out, lse
 
 
-def roofline_hbm(nbytes, ms, kind, workload, split):
-    """Decode roofline; `split` says whether the launch ran split groups (then a
-    combine kernel follows the decode kernel and both are timed)."""
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    traffic = traffic_for(kind, workload)
-    per_launch = {"algorithmic_bytes": nbytes, "avg_ms": round(ms, 5)}
-    if traffic is not None:  # measured DRAM bytes at the same rate: the real HBM load
-        per_launch["dram_gbs"] = round(traffic / (ms * 1e-3) / 1e9, 1)
-    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "decode_bf16_kernel + decode_combine_kernel" if split else "decode_bf16_kernel",
-            "per_launch": per_launch}
+class OraclePool:
+    """Process pool over the visible host cores, forked before any GPU call."""
 
+    def __init__(self):
+        import multiprocessing as mp
+        self.cores = len(os.sched_getaffinity(0))
+        self.pool = mp.get_context("fork").Pool(self.cores, initializer=_oracle_worker_init)
 
-def roofline_mfma(flops, ms, kind, workload):
-    tfs = flops / (ms * 1e-3) / 1e12
-    return {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
-            "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
-            "traffic": traffic_for(kind, workload), "kernel": "prefill_bf16_kernel",
-            "per_launch": {"algorithmic_flops": flops, "avg_ms": round(ms, 5)}}
+    def decode(self, key, requests):
+        t0 = time.perf_counter()
+        res = self.pool.map(_oracle_decode_one, [(key, r) for r in requests], chunksize=1)
+        return {r: (o, l) for r, o, l in res}, time.perf_counter() - t0
+
+    def prefill(self, key, rows_by_req):
+        t0 = time.perf_counter()
+        jobs = [(key, r, rows[i:i + 8]) for r, rows in rows_by_req.items()
+                for i in range(0, len(rows), 8)]
+        res = self.pool.map(_oracle_prefill_rows, jobs, chunksize=1)
+        out = {}
+        for r, rows, o, l in res:
+            out.setdefault(r, []).append((rows, o, l))
+        return out, time.perf_counter() - t0
+
+    def close(self):
+        self.pool.terminate()
+        self.pool.join()
 
 
 def _cpu_model():
@@ -190,46 +139,163 @@ def _cpu_model():
     return "unknown"
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the headline workload.
+def _errors(gpu, ref):
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    return float(np.max(np.abs(g - r))), float(np.linalg.norm(g - r) / np.linalg.norm(r))
 
-    Requests (decode) or 16-row slices of new tokens (prefill) are run in turn
-    until about budget_s seconds of single-threaded CPU work are done.
-    """
-    from threadpoolctl import threadpool_limits
 
-    from oracle import run_decode, run_prefill
-    t0 = time.perf_counter()
-    work = 0
-    units = 0
-    with threadpool_limits(limits=1):
-        if w.kind == "decode":
-            keys = w.keys_per_request()
-            while time.perf_counter() - t0 < budget_s or units < 2:
-                r = units % w.batch
-                run_decode(w, requests=[r])
-                work += int(keys[r]) * w.num_kv_heads * w.head_dim * 2 * 2
-                units += 1
-            dt = time.perf_counter() - t0
-            return {"value": round(work / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-                    "kind": "oracle", "cpu_model": _cpu_model(),
-                    "visible_cores": len(os.sched_getaffinity(0)),
-                    "sample": f"{units} decode requests (cycling over the {w.batch}-request "
-                              f"batch), fp64 NumPy, BLAS limited to 1 thread, {dt:.1f} s"}
-        cached = w.keys_per_request() - np.array([w.q_len(r) for r in range(w.batch)])
-        while time.perf_counter() - t0 < budget_s or units < 1:
-            r = units % w.batch
-            rows = np.arange(16 * (units // w.batch) % w.q_len(r), w.q_len(r))[:16]
-            run_prefill(w, requests=[r], rows={r: rows})
-            work += int(sum(4 * w.head_dim * w.num_q_heads * (int(cached[r]) + int(j) + 1)
-                            for j in rows))
-            units += 1
-        dt = time.perf_counter() - t0
-        return {"value": round(work / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-                "kind": "oracle", "cpu_model": _cpu_model(),
-                "visible_cores": len(os.sched_getaffinity(0)),
-                "sample": f"{units} slices of 16 new-token rows, fp64 NumPy, BLAS limited to "
-                          f"1 thread, {dt:.1f} s"}
+def _parity(gpu_rows, ref_rows, what):
+    max_abs, rel = _errors(np.concatenate([g.reshape(-1) for g in gpu_rows]),
+                           np.concatenate([r.reshape(-1) for r in ref_rows]))
+    ok = bool(np.all(np.isfinite(np.concatenate([g.reshape(-1) for g in gpu_rows])))
+              and max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2)
+    return {"checked": what, "max_abs": float(f"{max_abs:.4g}"), "rel_l2": float(f"{rel:.4g}"),
+            "tolerance": {"max_abs": BF16_MAX_ABS, "rel_l2": BF16_REL_L2}, "pass": ok}
+
+
+# --------------------------------------------------------------------- timing
+def time_launches(run, steps, warmup, stream, flush=None, min_warm_s=WARM_S):
+    """Warm up (at least `warmup` launches and `min_warm_s` seconds of them), then
+    time exactly `steps` back-to-back launches by wall clock, and `steps` more
+    with per-launch HIP events on the launch stream (optionally each after
+    `flush()`).  Returns a dict of the figures and the warm-up launches run."""
+    import torch
+    t_warm = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t_warm < min_warm_s:
+        run()
+        done += 1
+        if done % 50 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    wall = None
+    if flush is None:
+        # Wall clock: exactly `steps` launches back to back, with nothing else
+        # on the stream (per-launch event records would add their own gaps).
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        if flush is not None:
+            flush()
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in evs])  # ms
+    return {"wall_s": wall, "mean": float(per.mean()), "median": float(np.median(per)),
+            "p10": float(np.percentile(per, 10)), "p90": float(np.percentile(per, 90)),
+            "warmup_launches": done}
+
+
+def make_flushers(nbytes=1 << 30):
+    """Two ways to evict the pool from L2 and the Infinity Cache between cold
+    repetitions: a read-only sweep of a 1 GiB buffer (leaves no dirty lines),
+    and a 1 GiB fill (whose dirty lines are written back while the next
+    launch runs)."""
+    import torch
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def read_sweep():
+        torch.sum(buf, dim=0, out=sink)
+
+    def write_fill():
+        buf.fill_(1.0)
+    return read_sweep, write_fill
+
+
+def _ms(x):
+    return round(x, 5)
+
+
+def run_decode_workload(w, k, v, stream, steps, warmup, split_blocks=0, cold=True):
+    from position_agnostic_kv_lazy_amd.prepare import prepare
+    db = prepare(w, k, v, split_blocks=split_blocks)
+    run = lambda: db.run(stream)  # noqa: E731
+    t = time_launches(run, steps, warmup, stream)
+    nbytes = w.logical_kv_bytes()
+    res = {
+        "logical_kv_bytes": nbytes,
+        "unique_kv_bytes": w.unique_kv_bytes(),
+        "warmup_launches": t["warmup_launches"],
+        "wall_ms_per_step": 1e3 * t["wall_s"] / steps,
+        "event_ms_mean": t["mean"], "event_ms_median": t["median"],
+        "event_ms_p10": t["p10"], "event_ms_p90": t["p90"],
+        "gbs_logical": nbytes / (t["mean"] * 1e-3) / 1e9,
+        "workspace_bytes": 0 if db.workspace is None else int(db.workspace.numel()),
+        "_db": db,
+    }
+    if cold:
+        read_sweep, write_fill = make_flushers()
+        n = max(5, steps // 2)
+        # right after the warm timing: the clocks are up, one warm-up launch suffices
+        c = time_launches(run, n, 1, stream, read_sweep, min_warm_s=0.0)
+        cw = time_launches(run, n, 1, stream, write_fill, min_warm_s=0.0)
+        res.update({
+            "cold_event_ms_mean": c["mean"], "cold_event_ms_median": c["median"],
+            "cold_gbs_logical": nbytes / (c["mean"] * 1e-3) / 1e9,
+            "cold_after_write_flush_event_ms_mean": cw["mean"],
+            "cold_after_write_flush_gbs_logical": nbytes / (cw["mean"] * 1e-3) / 1e9,
+            "cold_flush": "1 GiB read-only sweep before each launch (primary); the "
+                          "write-flush figure fills 1 GiB instead, whose dirty lines are "
+                          "written back during the timed launch",
+        })
+        del read_sweep, write_fill
+    return res
+
+
+def run_prefill_workload(w, k, v, stream, steps, warmup):
+    from position_agnostic_kv_lazy_amd.prepare import prepare
+    db = prepare(w, k, v)
+    run = lambda: db.run(stream)  # noqa: E731
+    t = time_launches(run, steps, warmup, stream)
+    flops = w.prefill_flops()
+    return {
+        "flops": flops,
+        "warmup_launches": t["warmup_launches"],
+        "wall_ms_per_step": 1e3 * t["wall_s"] / steps,
+        "event_ms_mean": t["mean"], "event_ms_median": t["median"],
+        "event_ms_p10": t["p10"], "event_ms_p90": t["p90"],
+        "tflops": flops / (t["mean"] * 1e-3) / 1e12,
+        "_db": db,
+    }
+
+
+def roofline_hbm(res, kind, workload, split):
+    """Decode HBM roofline on the bytes HBM delivers per launch (rocprofv3
+    counters, same kernel source) over the launch time by HIP events."""
+    ms = res["event_ms_mean"]
+    traffic = traffic_for(kind, workload)
+    kern = "decode_bf16_kernel + decode_combine_kernel" if split else "decode_bf16_kernel"
+    per_launch = {"algorithmic_bytes": res["logical_kv_bytes"],
+                  "unique_bytes": res["unique_kv_bytes"],
+                  "logical_gbs": round(res["logical_kv_bytes"] / (ms * 1e-3) / 1e9, 1),
+                  "avg_ms": _ms(ms)}
+    if traffic is None:
+        # no counter record for this kernel source: the logical rate is all we have
+        return {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": None, "traffic": None, "kernel": kern,
+                "basis": "no HBM counter record for this kernel source", "per_launch": per_launch}
+    gbs = traffic / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kern,
+            "basis": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE, "
+                     "profiles/traffic.json) / HIP-event launch time",
+            "per_launch": per_launch}
+
+
+def roofline_mfma(flops, ms, kind, workload):
+    tfs = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
+            "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+            "traffic": traffic_for(kind, workload), "kernel": "prefill_bf16_kernel",
+            "per_launch": {"algorithmic_flops": flops, "avg_ms": _ms(ms)}}
 
 
 def _clean(res):
@@ -237,7 +303,8 @@ def _clean(res):
             for kk, vv in res.items() if not kk.startswith("_")}
 
 
-def _extra_no_sharing(stream, steps):
+# ---------------------------------------------------------------- extra legs
+def _extra_no_sharing(stream, steps, warmup):
     """Control for the shared-document mix: configuration 2's shapes with every
     request reading its own documents, so logical bytes = unique bytes = what
     DRAM must deliver."""
@@ -247,74 +314,108 @@ def _extra_no_sharing(stream, steps):
         log("no-sharing control (64 requests x 10 private documents)")
         w = make_no_sharing_decode()
         k, v = upload_pool(w.k_pool, w.v_pool)
-        res = run_decode_workload(w, k, v, stream, steps, 3)
+        res = run_decode_workload(w, k, v, stream, steps, warmup)
         out = _clean(res)
         out["frac_of_hbm_peak"] = round(res["gbs_logical"] / HBM_PEAK_GBS, 4)
         out["cold_frac_of_hbm_peak"] = round(res["cold_gbs_logical"] / HBM_PEAK_GBS, 4)
+        out["cold_after_write_flush_frac_of_hbm_peak"] = round(
+            res["cold_after_write_flush_gbs_logical"] / HBM_PEAK_GBS, 4)
         return {w.name: out}
     except Exception as e:  # reported, never hidden
-        return {"no_sharing_control": {"error": repr(e)}}
+        return {"llama3_8b_decode_no_sharing": {"error": repr(e)}}
 
 
-def _extra_achievable(stream):
+def _extra_achievable(stream, steps, warmup):
     """Reference rates measured on the same GPU in the same run: a plain 1 GiB
-    device copy (torch copy_) and a plain bf16 GEMM (torch.matmul, 8192^3)."""
+    device copy (torch copy_), a 1 GiB read-only sweep (torch sum) and a plain
+    bf16 GEMM (torch.matmul, 8192^3)."""
     import torch
     try:
-        log("achievable references: 1 GiB copy, 8192^3 bf16 GEMM")
+        log("achievable references: 1 GiB copy and read, 8192^3 bf16 GEMM")
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
-        _, copy_ms, _, _ = time_launches(lambda: dst.copy_(src), 10, 3, stream,
-                                         min_warm_s=WARM_S)
-        del src, dst
+        copy = time_launches(lambda: dst.copy_(src), steps, warmup, stream)
+        del dst
+        srcf = src.view(torch.float32)
+        sink = torch.empty((), dtype=torch.float32, device="cuda")
+        rd = time_launches(lambda: torch.sum(srcf, dim=0, out=sink), steps, warmup, stream)
+        del src, srcf
         n = 8192
         a = torch.randn(n, n, device="cuda").to(torch.bfloat16).contiguous()
         b = torch.randn(n, n, device="cuda").to(torch.bfloat16).contiguous()
         c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
-        _, gemm_ms, _, _ = time_launches(lambda: torch.matmul(a, b, out=c), 10, 3, stream,
-                                         min_warm_s=WARM_S)
+        gemm = time_launches(lambda: torch.matmul(a, b, out=c), steps, warmup, stream)
         del a, b, c
         torch.cuda.empty_cache()
         return {"achievable_references": {
-            "copy_1gib_gbs_moved": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
-            "gemm_bf16_8192_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
-            "note": "plain copy reads + writes 1 GiB; GEMM through torch.matmul (hipBLASLt)"}}
+            "copy_1gib_gbs_moved": round(2 * (1 << 30) / (copy["mean"] * 1e-3) / 1e9, 1),
+            "read_1gib_gbs": round((1 << 30) / (rd["mean"] * 1e-3) / 1e9, 1),
+            "gemm_bf16_8192_tflops": round(2 * n ** 3 / (gemm["mean"] * 1e-3) / 1e12, 1),
+            "note": "plain copy reads + writes 1 GiB; read = torch.sum over 1 GiB; GEMM "
+                    "through torch.matmul (hipBLASLt)"}}
     except Exception as e:  # reported, never hidden
         return {"achievable_references": {"error": repr(e)}}
 
 
-def _extra_prefill(stream, steps):
+def _extra_prefill(w3, stream, steps, warmup, oracle):
+    """Config 3 prefill against the MFMA roofline; sampled rows of the timed
+    launch's output are checked against the oracle, which is timed too."""
     from position_agnostic_kv_lazy_amd.prepare import upload_pool
-    from workloads import make_config
     try:
         log("prefill (Llama-3-8B shapes, 8 requests x 10240 cached + 512 new)")
-        w3 = make_config(3)
         k3, v3 = upload_pool(w3.k_pool, w3.v_pool)
-        r3 = run_prefill_workload(w3, k3, v3, stream, steps, 3)
+        r3 = run_prefill_workload(w3, k3, v3, stream, steps, warmup)
         out = _clean(r3)
         out["roofline"] = roofline_mfma(r3["flops"], r3["event_ms_mean"], "prefill", w3.name)
+        if oracle is not None:
+            import torch
+            torch.cuda.synchronize()
+            got = r3["_db"].out_f32()
+            # 64 rows per request: spread over the new tokens, first and last included
+            rows = {r: np.unique(np.linspace(0, w3.q_len(r) - 1, 64).astype(np.int64))
+                    for r in range(w3.batch)}
+            log(f"oracle: prefill rows ({sum(len(x) for x in rows.values())}) on "
+                f"{oracle.cores} cores")
+            ref, dt = oracle.prefill("prefill", rows)
+            g_rows, r_rows, flops = [], [], 0
+            cached = w3.keys_per_request() - np.array([w3.q_len(r) for r in range(w3.batch)])
+            for r, parts in ref.items():
+                a = int(w3.cu_q[r])
+                for rr, o, _ in parts:
+                    g_rows.append(got[a + np.asarray(rr)])
+                    r_rows.append(o)
+                    flops += sum(4 * w3.head_dim * w3.num_q_heads * (int(cached[r]) + int(j) + 1)
+                                 for j in rr)
+            out["parity_vs_oracle"] = _parity(g_rows, r_rows,
+                                              f"{sum(len(x) for x in rows.values())} sampled "
+                                              f"new-token rows (all heads) of the timed launch")
+            out["cpu_baseline"] = {
+                "value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.cores,
+                "kind": "oracle", "cpu_model": _cpu_model(),
+                "sample": f"{sum(len(x) for x in rows.values())} new-token rows (64 per "
+                          f"request, all 32 heads) of the prefill batch, fp64 NumPy, "
+                          f"{oracle.cores} worker processes x 1 BLAS thread, {dt:.1f} s"}
         return {w3.name: out}
     except Exception as e:  # reported, never hidden
         return {"llama3_8b_prefill": {"error": repr(e)}}
 
 
-def _extra_long_decode(stream, steps):
+def _extra_long_decode(stream, steps, warmup):
     from position_agnostic_kv_lazy_amd.prepare import upload_pool
     from workloads import make_config
     try:
         log("long-context decode (16 requests x 64K keys)")
         w4 = make_config(4)
         k4, v4 = upload_pool(w4.k_pool, w4.v_pool)
-        r4 = run_decode_workload(w4, k4, v4, stream, steps, 3)
+        r4 = run_decode_workload(w4, k4, v4, stream, steps, warmup)
         out = _clean(r4)
-        out["roofline"] = roofline_hbm(r4["logical_kv_bytes"], r4["event_ms_mean"], "decode",
-                                       w4.name, r4["workspace_bytes"] > 0)
+        out["roofline"] = roofline_hbm(r4, "decode", w4.name, r4["workspace_bytes"] > 0)
         return {w4.name: out}
     except Exception as e:  # reported, never hidden
         return {"long_decode": {"error": repr(e)}}
 
 
-def _extra_mixed(stream, steps):
+def _extra_mixed(stream, steps, warmup):
     """Config 5: one decode launch and one prefill launch on one shared pool."""
     import torch
 
@@ -332,36 +433,41 @@ def _extra_mixed(stream, steps):
             ev = torch.cuda.Event()
             ev.record(stream)
             s2.wait_event(ev)
-            dp.run(s2)
-            dd.run(stream)
+            dd.run(s2)
+            dp.run(stream)
             e2 = torch.cuda.Event()
             e2.record(s2)
             stream.wait_event(e2)
 
         def pair_serial():
-            dp.run(stream)
             dd.run(stream)
+            dp.run(stream)
 
-        _, p2, _, _ = time_launches(pair_two_streams, steps, 3, stream, min_warm_s=WARM_S)
-        _, p1, _, _ = time_launches(pair_serial, steps, 3, stream, min_warm_s=WARM_S)
-        _, dm, _, _ = time_launches(lambda: dd.run(stream), steps, 3, stream, min_warm_s=WARM_S)
-        _, fm, _, _ = time_launches(lambda: dp.run(stream), steps, 3, stream, min_warm_s=WARM_S)
+        p2 = time_launches(pair_two_streams, steps, warmup, stream)
+        p1 = time_launches(pair_serial, steps, warmup, stream)
+        dm = time_launches(lambda: dd.run(stream), steps, warmup, stream)
+        fm = time_launches(lambda: dp.run(stream), steps, warmup, stream)
         nb = m5.decode.logical_kv_bytes()
         fl = m5.prefill.prefill_flops()
         return {"mixed_step": {
-            "pair_serial_event_ms_mean": round(p1, 5),
-            "pair_two_streams_event_ms_mean": round(p2, 5),
-            "decode_event_ms_mean": round(dm, 5),
-            "prefill_event_ms_mean": round(fm, 5),
-            "decode_gbs_logical": round(nb / (dm * 1e-3) / 1e9, 1),
-            "prefill_tflops": round(fl / (fm * 1e-3) / 1e12, 1),
-            "decode_logical_kv_bytes": nb, "prefill_flops": fl,
+            "pair_serial_event_ms_mean": _ms(p1["mean"]),
+            "pair_two_streams_event_ms_mean": _ms(p2["mean"]),
+            "decode_event_ms_mean": _ms(dm["mean"]),
+            "prefill_event_ms_mean": _ms(fm["mean"]),
+            "decode_gbs_logical": round(nb / (dm["mean"] * 1e-3) / 1e9, 1),
+            "prefill_tflops": round(fl / (fm["mean"] * 1e-3) / 1e12, 1),
+            "decode_logical_kv_bytes": nb, "decode_unique_kv_bytes": m5.decode.unique_kv_bytes(),
+            "prefill_flops": fl,
+            "warmup_launches": {"pair_two_streams": p2["warmup_launches"],
+                                "pair_serial": p1["warmup_launches"],
+                                "decode": dm["warmup_launches"],
+                                "prefill": fm["warmup_launches"]},
         }}
     except Exception as e:
         return {"mixed_step": {"error": repr(e)}}
 
 
-def _extra_rotation_ablation(w, k, v, stream, steps, pf_out):
+def _extra_rotation_ablation(w, k, v, stream, steps, warmup, pf_out):
     """Where deferred RoPE stands against the alternatives, on the headline decode batch.
 
     * doc_local: each distinct document written once with its keys pre-rotated
@@ -374,8 +480,12 @@ def _extra_rotation_ablation(w, k, v, stream, steps, pf_out):
       every segment start 0: no key rotation and one q rotation per request --
       the rotation-off baseline.  The copy itself is timed too: its bytes are
       the read-modify-write the shared position-free pool never does.
-    All three outputs are compared with the position-free path's output.
+    * alibi: the same shared pool, no rotation at all.
+    All outputs are compared with the position-free path's output.  Every
+    leg uses the same warm-up rule as the headline.
     """
+    import copy
+
     import torch
 
     from position_agnostic_kv_lazy_amd import binding as B
@@ -400,10 +510,10 @@ def _extra_rotation_ablation(w, k, v, stream, steps, pf_out):
 
     def decode(wx, kd, vd):
         db = prepare(wx, kd, vd, pool_mode="doc_local", max_pos=rows)
-        _, ms, _, _ = time_launches(lambda: db.run(stream), steps, 3, stream, min_warm_s=WARM_S)
+        t = time_launches(lambda: db.run(stream), steps, warmup, stream)
         torch.cuda.synchronize()
         diff = float((db.out.view(torch.bfloat16).float() - pos_free).abs().max())
-        return db, ms, diff
+        return t, diff
 
     nbytes = w.logical_kv_bytes()
     # ---- document-local pool
@@ -411,15 +521,15 @@ def _extra_rotation_ablation(w, k, v, stream, steps, pf_out):
     kt, vt = gather(slots)
     kd, vd = torch.zeros_like(k), torch.zeros_like(v)
     p_w = params_for(w, int(k.shape[0]), rows)
-    run_w = store(p_w, kt, vt, slots, idx, kd, vd)
-    _, wms, _, _ = time_launches(run_w, max(3, steps // 4), 1, stream, min_warm_s=WARM_S)
+    tw = time_launches(store(p_w, kt, vt, slots, idx, kd, vd), max(3, steps // 4), 1, stream)
     moved = 4 * len(slots) * Hkv * D * 2
-    _, dms, diff = decode(w, kd, vd)
+    td, diff = decode(w, kd, vd)
     res["doc_local"] = {
-        "decode_event_ms_mean": round(dms, 5),
-        "decode_gbs_logical": round(nbytes / (dms * 1e-3) / 1e9, 1),
-        "write_tokens": int(len(slots)), "write_event_ms_mean": round(wms, 5),
-        "write_gbs": round(moved / (wms * 1e-3) / 1e9, 1),
+        "decode_event_ms_mean": _ms(td["mean"]),
+        "decode_gbs_logical": round(nbytes / (td["mean"] * 1e-3) / 1e9, 1),
+        "decode_warmup_launches": td["warmup_launches"],
+        "write_tokens": int(len(slots)), "write_event_ms_mean": _ms(tw["mean"]),
+        "write_gbs": round(moved / (tw["mean"] * 1e-3) / 1e9, 1),
         "max_abs_diff_vs_position_free": diff}
     del kt, vt, kd, vd
     torch.cuda.empty_cache()
@@ -431,19 +541,18 @@ def _extra_rotation_ablation(w, k, v, stream, steps, pf_out):
     km = torch.zeros((nb_m,) + tuple(k.shape[1:]), dtype=k.dtype, device=k.device)
     vm = torch.zeros((nb_m,) + tuple(v.shape[1:]), dtype=v.dtype, device=v.device)
     p_m = params_for(w, nb_m, rows)
-    run_m = store(p_m, kt, vt, dst, pos, km, vm)
-    _, mms, _, _ = time_launches(run_m, max(3, steps // 4), 1, stream, min_warm_s=WARM_S)
+    tm = time_launches(store(p_m, kt, vt, dst, pos, km, vm), max(3, steps // 4), 1, stream)
     moved = 4 * len(dst) * Hkv * D * 2
-    import copy
     wm = copy.copy(w)
     wm.requests = reqs
-    _, rms, diff = decode(wm, km, vm)
+    tr, diff = decode(wm, km, vm)
     res["materialised"] = {
-        "decode_event_ms_mean": round(rms, 5),
-        "decode_gbs_logical": round(nbytes / (rms * 1e-3) / 1e9, 1),
-        "copy_tokens": int(len(dst)), "copy_event_ms_mean": round(mms, 5),
-        "copy_gbs": round(moved / (mms * 1e-3) / 1e9, 1),
-        "copy_plus_decode_ms": round(mms + rms, 5),
+        "decode_event_ms_mean": _ms(tr["mean"]),
+        "decode_gbs_logical": round(nbytes / (tr["mean"] * 1e-3) / 1e9, 1),
+        "decode_warmup_launches": tr["warmup_launches"],
+        "copy_tokens": int(len(dst)), "copy_event_ms_mean": _ms(tm["mean"]),
+        "copy_gbs": round(moved / (tm["mean"] * 1e-3) / 1e9, 1),
+        "copy_plus_decode_ms": _ms(tm["mean"] + tr["mean"]),
         "pool_bytes": int(km.numel() * 2 * 2), "shared_pool_bytes": int(k.numel() * 2 * 2),
         "max_abs_diff_vs_position_free": diff}
     del kt, vt, km, vm
@@ -451,12 +560,14 @@ def _extra_rotation_ablation(w, k, v, stream, steps, pf_out):
 
     # ---- ALiBi (score-space positional method, no rotation) on the position-free pool
     db = prepare(w, k, v, pos_encoding="alibi", max_pos=rows)
-    _, ams, _, _ = time_launches(lambda: db.run(stream), steps, 3, stream, min_warm_s=WARM_S)
-    res["alibi"] = {"decode_event_ms_mean": round(ams, 5),
-                    "decode_gbs_logical": round(nbytes / (ams * 1e-3) / 1e9, 1)}
+    ta = time_launches(lambda: db.run(stream), steps, warmup, stream)
+    res["alibi"] = {"decode_event_ms_mean": _ms(ta["mean"]),
+                    "decode_gbs_logical": round(nbytes / (ta["mean"] * 1e-3) / 1e9, 1),
+                    "decode_warmup_launches": ta["warmup_launches"]}
     return res
 
 
+# ----------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -464,7 +575,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4],
                     help="headline workload: 2 decode (default), 3 prefill, 4 long decode")
-    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma-separated subset of " + ",".join(LEGS))
+    ap.add_argument("--no-extra", action="store_true", help="headline leg only")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--split-blocks", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -474,11 +587,30 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    legs = {"headline"} if args.no_extra else set(x for x in args.legs.split(",") if x)
+    unknown = legs - set(LEGS)
+    if unknown:
+        print(f"unknown legs {sorted(unknown)}", file=sys.stderr)
+        sys.exit(2)
+
+    from workloads import make_config
+
+    # CPU side first: the workloads the oracle checks, then the oracle's worker
+    # processes, forked before this process makes any GPU call.
+    log(f"generating config {args.config}")
+    w = make_config(args.config)
+    w3 = None
+    if "prefill" in legs and args.config != 3:
+        w3 = make_config(3)
+    oracle = None
+    if not args.no_cpu:
+        _ORACLE_W["headline"] = w
+        _ORACLE_W["prefill"] = w3 if w3 is not None else w
+        oracle = OraclePool()
 
     import torch
 
     from position_agnostic_kv_lazy_amd.prepare import upload_pool
-    from workloads import make_config
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     stream = torch.cuda.current_stream()
@@ -491,41 +623,71 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    log(f"generating config {args.config}")
-    w = make_config(args.config)
     k, v = upload_pool(w.k_pool, w.v_pool)
     wl_name = w.name
     config = {"workload": wl_name, "batch": w.batch, "q_heads": w.num_q_heads,
               "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
               "docs": "Zipf document mix, shared physical blocks"}
+    steps2 = max(5, args.steps // 2)
+    extra = {}
     ablation = None
     if w.kind == "decode":
         log("timing headline decode")
-        main_res = run_decode_workload(w, k, v, stream, args.steps, args.warmup, args.split_blocks,
-                                       min_warm_s=0.0)
-        if not args.no_extra:
-            log("rotation ablation: doc-local pool and materialised copies")
+        main_res = run_decode_workload(w, k, v, stream, args.steps, args.warmup, args.split_blocks)
+        torch.cuda.synchronize()
+        head_out = main_res["_db"].out_f32()
+        if "ablation" in legs:
+            log("rotation ablation: doc-local pool, materialised copies, ALiBi")
             try:
-                ablation = _extra_rotation_ablation(w, k, v, stream, max(5, args.steps // 2),
+                ablation = _extra_rotation_ablation(w, k, v, stream, steps2, args.warmup,
                                                     main_res["_db"].out.view(torch.bfloat16))
-                ablation["position_free_decode_event_ms_mean"] = round(main_res["event_ms_mean"],
-                                                                       5)
+                ablation["position_free_decode_event_ms_mean"] = _ms(main_res["event_ms_mean"])
             except Exception as e:  # reported, never hidden
                 ablation = {"error": repr(e)}
             torch.cuda.empty_cache()
         ms = main_res["wall_ms_per_step"]
         value, unit = main_res["logical_kv_bytes"] / (ms * 1e-3) / 1e9, "GB/s"
         config["keys_per_request"] = int(w.keys_per_request()[0])
-        roof = roofline_hbm(main_res["logical_kv_bytes"], main_res["event_ms_mean"], "decode",
-                            wl_name, main_res["workspace_bytes"] > 0)
+        roof = roofline_hbm(main_res, "decode", wl_name, main_res["workspace_bytes"] > 0)
     else:
         log("timing headline prefill")
-        main_res = run_prefill_workload(w, k, v, stream, args.steps, args.warmup, min_warm_s=0.0)
+        main_res = run_prefill_workload(w, k, v, stream, args.steps, args.warmup)
+        head_out = None
         ms = main_res["wall_ms_per_step"]
         value, unit = main_res["flops"] / (ms * 1e-3) / 1e12, "TFLOP/s"
         config["new_tokens_per_request"] = int(w.q_len(0))
         config["cached_keys_per_request"] = int(w.keys_per_request()[0] - w.q_len(0))
         roof = roofline_mfma(main_res["flops"], main_res["event_ms_mean"], "prefill", wl_name)
+    extra[wl_name] = _clean(main_res)
+    if ablation is not None:
+        extra["rotation_ablation"] = ablation
+    del main_res, k, v
+    torch.cuda.empty_cache()
+
+    if "prefill" in legs and args.config != 3:
+        extra.update(_extra_prefill(w3, stream, steps2, args.warmup, oracle))
+        torch.cuda.empty_cache()
+    if "long_decode" in legs and args.config != 4:
+        extra.update(_extra_long_decode(stream, steps2, args.warmup))
+        torch.cuda.empty_cache()
+    if "mixed" in legs:
+        extra.update(_extra_mixed(stream, steps2, args.warmup))
+        torch.cuda.empty_cache()
+    if "no_sharing" in legs and args.config == 2:
+        extra.update(_extra_no_sharing(stream, steps2, args.warmup))
+        torch.cuda.empty_cache()
+        ns = extra.get("llama3_8b_decode_no_sharing", {})
+        if "frac_of_hbm_peak" in ns:
+            roof["controls"] = {
+                "no_sharing_warm_frac": ns["frac_of_hbm_peak"],
+                "no_sharing_cold_frac": ns["cold_frac_of_hbm_peak"],
+                "no_sharing_cold_after_write_flush_frac":
+                    ns["cold_after_write_flush_frac_of_hbm_peak"],
+                "note": "configuration 2's shapes with no document shared: logical = unique "
+                        "bytes = what HBM must deliver; cold = after a 1 GiB read-only sweep"}
+    if "references" in legs:
+        extra.update(_extra_achievable(stream, 10, 3))
+
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -542,31 +704,22 @@ def main():
         "config": config,
         "roofline": roof,
     }
-    extra = {wl_name: _clean(main_res)}
-    if ablation is not None:
-        extra["rotation_ablation"] = ablation
-    del main_res, k, v
-    torch.cuda.empty_cache()
 
-    if not args.no_extra:
-        steps2 = max(5, args.steps // 2)
-        if args.config != 3:
-            extra.update(_extra_prefill(stream, steps2))
-            torch.cuda.empty_cache()
-        if args.config != 4:
-            extra.update(_extra_long_decode(stream, steps2))
-            torch.cuda.empty_cache()
-        extra.update(_extra_mixed(stream, steps2))
-        torch.cuda.empty_cache()
-        if args.config == 2:
-            extra.update(_extra_no_sharing(stream, steps2))
-            torch.cuda.empty_cache()
-        extra.update(_extra_achievable(stream))
+    if oracle is not None:
+        if w.kind == "decode":
+            log(f"oracle: all {w.batch} headline requests on {oracle.cores} cores")
+            ref, dt = oracle.decode("headline", range(w.batch))
+            result["parity_vs_oracle"] = _parity(
+                [head_out[r] for r in range(w.batch)], [ref[r][0] for r in range(w.batch)],
+                f"all {w.batch} requests x {w.num_q_heads} heads of the timed headline launch")
+            result["cpu_baseline"] = {
+                "value": round(w.logical_kv_bytes() / dt / 1e9, 4), "unit": "GB/s",
+                "cores": oracle.cores, "kind": "oracle", "cpu_model": _cpu_model(),
+                "sample": f"the whole headline batch ({w.batch} requests, "
+                          f"{int(w.keys_per_request().sum())} keys), fp64 NumPy, "
+                          f"{oracle.cores} worker processes x 1 BLAS thread, {dt:.2f} s"}
+        oracle.close()
     result["extra"] = extra
-
-    if not args.no_cpu:
-        log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result), flush=True)
 
 

@@ -161,6 +161,19 @@ class Workload:
         elem = 2 if self.is_bf16() else 4
         return int(self.keys_per_request().sum()) * self.num_kv_heads * self.head_dim * 2 * elem
 
+    def unique_kv_bytes(self) -> int:
+        """K+V bytes of the distinct pool blocks the tables touch, each counted once
+        with its valid slots: what HBM must deliver at least when every shared
+        block is read once per launch."""
+        elem = 2 if self.is_bf16() else 4
+        tokens = {}
+        for segs in self.requests:
+            for s in segs:
+                for k, b in enumerate(np.asarray(s.blocks).ravel()):
+                    nv = min(self.block_size, int(s.n_tokens) - k * self.block_size)
+                    tokens[int(b)] = max(tokens.get(int(b), 0), nv)
+        return int(sum(tokens.values())) * self.num_kv_heads * self.head_dim * 2 * elem
+
     def prefill_flops(self) -> int:
         """4*D*Hq per unmasked (query, key) pair, summed over all new tokens."""
         assert self.kind == "prefill"
