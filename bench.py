@@ -623,7 +623,6 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    k, v = upload_pool(w.k_pool, w.v_pool)
     wl_name = w.name
     config = {"workload": wl_name, "batch": w.batch, "q_heads": w.num_q_heads,
               "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
@@ -631,7 +630,12 @@ def main():
     steps2 = max(5, args.steps // 2)
     extra = {}
     ablation = None
-    if w.kind == "decode":
+    value = ms = roof = head_out = None
+    unit = "GB/s" if w.kind == "decode" else "TFLOP/s"
+    if "headline" not in legs:
+        log("headline leg skipped (--legs): value and roofline are null")
+    elif w.kind == "decode":
+        k, v = upload_pool(w.k_pool, w.v_pool)
         log("timing headline decode")
         main_res = run_decode_workload(w, k, v, stream, args.steps, args.warmup, args.split_blocks)
         torch.cuda.synchronize()
@@ -650,6 +654,7 @@ def main():
         config["keys_per_request"] = int(w.keys_per_request()[0])
         roof = roofline_hbm(main_res, "decode", wl_name, main_res["workspace_bytes"] > 0)
     else:
+        k, v = upload_pool(w.k_pool, w.v_pool)
         log("timing headline prefill")
         main_res = run_prefill_workload(w, k, v, stream, args.steps, args.warmup)
         head_out = None
@@ -658,10 +663,11 @@ def main():
         config["new_tokens_per_request"] = int(w.q_len(0))
         config["cached_keys_per_request"] = int(w.keys_per_request()[0] - w.q_len(0))
         roof = roofline_mfma(main_res["flops"], main_res["event_ms_mean"], "prefill", wl_name)
-    extra[wl_name] = _clean(main_res)
+    if "headline" in legs:
+        extra[wl_name] = _clean(main_res)
+        del main_res, k, v
     if ablation is not None:
         extra["rotation_ablation"] = ablation
-    del main_res, k, v
     torch.cuda.empty_cache()
 
     if "prefill" in legs and args.config != 3:
@@ -677,7 +683,7 @@ def main():
         extra.update(_extra_no_sharing(stream, steps2, args.warmup))
         torch.cuda.empty_cache()
         ns = extra.get("llama3_8b_decode_no_sharing", {})
-        if "frac_of_hbm_peak" in ns:
+        if "frac_of_hbm_peak" in ns and roof is not None:
             roof["controls"] = {
                 "no_sharing_warm_frac": ns["frac_of_hbm_peak"],
                 "no_sharing_cold_frac": ns["cold_frac_of_hbm_peak"],
@@ -690,12 +696,12 @@ def main():
 
     result = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": None if value is None else round(value, 1),
         "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": None if ms is None else round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -706,7 +712,7 @@ def main():
     }
 
     if oracle is not None:
-        if w.kind == "decode":
+        if w.kind == "decode" and head_out is not None:
             log(f"oracle: all {w.batch} headline requests on {oracle.cores} cores")
             ref, dt = oracle.decode("headline", range(w.batch))
             result["parity_vs_oracle"] = _parity(
