@@ -380,6 +380,74 @@ LA_API la_status lazy_attn_decode_noalloc(const la_params* p, const void* q, con
                                           void* stream);
 
 /*
+ * Shared-segment decode (document-major split-KV).  A position-free pool lets
+ * one physical copy of a document serve every request that lists it, at any
+ * offset (§1; the same document at different offsets within one batch, §3).
+ * This decode also READS each such copy once per launch for all of them: a
+ * work item is a chunk of one distinct segment (a run of blocks several
+ * requests list identically) together with up to 32 / G of the requests
+ * holding it.  Keys are rotated by their index t within the segment, each
+ * request's query once per item by m - s (score = (R_{m-s} q)^T (R_t k), the
+ * per-document query rotation of §3.2 "Decoding", Eq. 6); a LA_POOL_DOC_LOCAL
+ * pool already stores R_t k and is read as stored.  Every (request, chunk)
+ * writes one fp32 partial (o, m, l) per query head; a second kernel merges
+ * each request's partials.  Same results as lazy_attn_decode (the softmax
+ * over exactly the listed keys) up to rounding order.
+ *
+ * lazy_attn_plan_shared_decode (host) builds the plan from the segment lists
+ * lazy_attn_pack_segments takes.  Two segments are the same when they have
+ * the same length and block list; their logical starts may differ.  The plan
+ * is a flat blob the caller copies to device memory as is:
+ *     int32x4 items[n_items]        {first word, blocks, first member, members}
+ *     int32x4 members[n_members]    {request, segment start s, partial slot, 0}
+ *     int32   req_part_start[batch + 1], padded to 16 bytes: request r owns
+ *                                   partial slots req_part_start[r] ..
+ *     uint64  words[n_words]        per chunk block: block id (bits 0..31),
+ *                                   index of slot 0 within the segment
+ *                                   (bits 32..55), n_valid - 1 (bits 56..62)
+ * It depends on the segments only (not on q_pos), so it can be reused while
+ * the tables do not change.
+ *   max_item_blocks  blocks per chunk (0 = 32); longer segments are cut
+ *   info             out: the sizes below
+ *   plan             host out, info->plan_bytes bytes; NULL = sizes only
+ *   plan_capacity    bytes available at plan
+ * bf16 only (LA_ERR_UNSUPPORTED for LA_FP32 and LA_ALIBI); the same checks
+ * as lazy_attn_pack_segments.
+ */
+typedef struct la_shared_plan_info {
+  int32_t batch;            /* requests the plan covers */
+  int32_t n_items;          /* work items; the launch runs n_items x num_kv_heads workgroups */
+  int32_t n_members;        /* (request, segment chunk) pairs = partial slots */
+  int32_t n_words;          /* block words of the distinct chunks */
+  int32_t members_per_item; /* at most 32 / (num_q_heads / num_kv_heads) */
+  int32_t max_item_blocks;  /* chunk length in blocks */
+  int64_t plan_bytes;       /* size of the plan blob */
+  int64_t workspace_bytes;  /* device workspace lazy_attn_decode_shared needs */
+} la_shared_plan_info;
+
+LA_API la_status lazy_attn_plan_shared_decode(
+    const la_params* p, int32_t batch, const int64_t* req_seg_start, const int64_t* seg_start,
+    const int64_t* seg_len, const uint8_t* seg_is_new, const int64_t* seg_blk_start,
+    const int64_t* seg_blocks, int32_t max_item_blocks, la_shared_plan_info* info, void* plan,
+    int64_t plan_capacity);
+
+/*
+ * Decode with a shared-segment plan (see above).
+ *   info       host: the plan's sizes, as lazy_attn_plan_shared_decode wrote them
+ *   plan       device copy of the plan blob, 16-byte aligned
+ *   q, k_pool, v_pool, q_pos, cos_sin, out, lse: as for lazy_attn_decode
+ *   workspace  device, >= info->workspace_bytes (the partials); clobbered
+ * Requires 0 <= s + t < max_pos for every key, m < max_pos, and a plan built
+ * for the same params and batch (not checked on the device).
+ */
+LA_API la_status lazy_attn_decode_shared(const la_params* p, const la_shared_plan_info* info,
+                                         const void* plan, const void* q, const void* k_pool,
+                                         const void* v_pool, const int32_t* q_pos,
+                                         const float* cos_sin, int32_t batch, void* out,
+                                         float* lse, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/*
  * Prefill: the new prompt tokens of each request attend every cached key of
  * the request and, among the new tokens, causally (§3.2 "Prefilling"; §3.4
  * Eq. 7 TTFT model: attention of the L' new tokens against all L keys).

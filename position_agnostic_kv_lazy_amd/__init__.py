@@ -30,6 +30,9 @@ from .binding import (  # noqa: F401
     lazy_attn_store_kv,
     lazy_attn_decode,
     lazy_attn_decode_noalloc,
+    lazy_attn_plan_shared_decode,
+    lazy_attn_decode_shared,
+    la_shared_plan_info,
     lazy_attn_prefill,
     lazy_attn_cache_simulate,
 )

@@ -51,6 +51,8 @@ EXPORTED = (
     "lazy_attn_store_kv",
     "lazy_attn_decode",
     "lazy_attn_decode_noalloc",
+    "lazy_attn_plan_shared_decode",
+    "lazy_attn_decode_shared",
     "lazy_attn_prefill",
     "lazy_attn_cache_simulate",
 )
@@ -84,6 +86,19 @@ class la_rope_scaling(ctypes.Structure):
         ("beta_fast", ctypes.c_double),
         ("beta_slow", ctypes.c_double),
         ("attn_factor", ctypes.c_double),
+    ]
+
+
+class la_shared_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_items", ctypes.c_int32),
+        ("n_members", ctypes.c_int32),
+        ("n_words", ctypes.c_int32),
+        ("members_per_item", ctypes.c_int32),
+        ("max_item_blocks", ctypes.c_int32),
+        ("plan_bytes", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -149,6 +164,15 @@ _lib.lazy_attn_decode.argtypes = [_prm, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int
 _lib.lazy_attn_decode_noalloc.restype = ctypes.c_int
 _lib.lazy_attn_decode_noalloc.argtypes = [_prm, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                           ctypes.c_int32, _P, _P, _P]
+_lib.lazy_attn_plan_shared_decode.restype = ctypes.c_int
+_lib.lazy_attn_plan_shared_decode.argtypes = [_prm, ctypes.c_int32, _i64p, _i64p, _i64p, _u8p,
+                                              _i64p, _i64p, ctypes.c_int32,
+                                              ctypes.POINTER(la_shared_plan_info), _P,
+                                              ctypes.c_int64]
+_lib.lazy_attn_decode_shared.restype = ctypes.c_int
+_lib.lazy_attn_decode_shared.argtypes = [_prm, ctypes.POINTER(la_shared_plan_info), _P, _P, _P,
+                                         _P, _P, _P, ctypes.c_int32, _P, _P, _P, ctypes.c_size_t,
+                                         _P]
 _lib.lazy_attn_cache_simulate.restype = ctypes.c_int
 _lib.lazy_attn_cache_simulate.argtypes = [ctypes.c_int64, _i64p, _i32p, ctypes.c_int32,
                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _i64p]
@@ -237,6 +261,52 @@ def lazy_attn_alibi_slopes(num_heads: int) -> np.ndarray:
     _check(_lib.lazy_attn_alibi_slopes(num_heads, out.ctypes.data_as(_f32p)),
            "lazy_attn_alibi_slopes")
     return out
+
+
+def _segment_arrays(requests):
+    """CSR arrays of segment lists (the layout lazy_attn_pack_segments takes)."""
+    req_seg, starts, lens, news, blk_start, blocks = [0], [], [], [], [0], []
+    for segs in requests:
+        for s in segs:
+            st, n, bl, nw = (s.start, s.n_tokens, s.blocks, s.is_new) if hasattr(s, "start") else s
+            starts.append(int(st))
+            lens.append(int(n))
+            news.append(1 if nw else 0)
+            bl = np.asarray(bl, dtype=np.int64).ravel()
+            blocks.append(bl)
+            blk_start.append(blk_start[-1] + len(bl))
+        req_seg.append(len(starts))
+    return (np.asarray(req_seg, np.int64), np.asarray(starts, np.int64),
+            np.asarray(lens, np.int64), np.asarray(news, np.uint8),
+            np.asarray(blk_start, np.int64),
+            np.concatenate(blocks).astype(np.int64) if blocks else np.zeros(0, np.int64))
+
+
+def lazy_attn_plan_shared_decode(params: la_params, requests: Sequence[Sequence],
+                                 max_item_blocks: int = 0):
+    """Shared-segment decode plan: (la_shared_plan_info, plan blob as uint8 numpy)."""
+    a_req, a_st, a_len, a_new, a_bs, a_bl = _segment_arrays(requests)
+    info = la_shared_plan_info()
+    args = (ctypes.byref(params), len(requests), a_req.ctypes.data_as(_i64p),
+            a_st.ctypes.data_as(_i64p), a_len.ctypes.data_as(_i64p), a_new.ctypes.data_as(_u8p),
+            a_bs.ctypes.data_as(_i64p), a_bl.ctypes.data_as(_i64p), int(max_item_blocks),
+            ctypes.byref(info))
+    _check(_lib.lazy_attn_plan_shared_decode(*args, None, 0), "lazy_attn_plan_shared_decode")
+    blob = np.zeros(int(info.plan_bytes), np.uint8)
+    _check(_lib.lazy_attn_plan_shared_decode(*args, blob.ctypes.data, blob.nbytes),
+           "lazy_attn_plan_shared_decode")
+    return info, blob
+
+
+def lazy_attn_decode_shared(params: la_params, info: la_shared_plan_info, plan, q, k_pool,
+                            v_pool, q_pos, cos_sin, batch: int, out, lse=None, workspace=None,
+                            stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.lazy_attn_decode_shared(ctypes.byref(params), ctypes.byref(info), _ptr(plan),
+                                        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(q_pos),
+                                        _ptr(cos_sin), batch, _ptr(out), _ptr(lse),
+                                        _ptr(workspace), ws_bytes, _stream(stream)),
+           "lazy_attn_decode_shared")
 
 
 def lazy_attn_pack_segments(params: la_params, requests: Sequence[Sequence]):

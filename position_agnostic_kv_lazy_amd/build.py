@@ -23,8 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblazyattn.so")
 
-SOURCES = ["lazy_attn_host.cpp", "attn_f32.hip", "decode_bf16.hip", "prefill_bf16.hip", "store_kv.hip",
-           "cache_sim.cpp"]
+SOURCES = ["lazy_attn_host.cpp", "attn_f32.hip", "decode_bf16.hip", "decode_shared_bf16.hip",
+           "prefill_bf16.hip", "store_kv.hip", "cache_sim.cpp"]
 ARCH = os.environ.get("LAZYATTN_ARCH", "gfx950")
 
 

@@ -1,0 +1,387 @@
+// bf16 shared-segment (document-major) split-KV decode over the paged pool (gfx950).
+//
+// The pool stores a document's keys without positions, so one physical copy
+// serves every request that lists the document, at whatever offset s the
+// request places it ("LazyAttention" §1 and §3.1 "Deferred encoding").  This
+// kernel also reads that copy once per launch for all of those requests: a
+// work item is a chunk of one distinct segment plus up to 32 / G requests
+// holding it, and one workgroup per (item, kv head) streams the chunk's K/V
+// blocks once and scores them against all of those requests' queries.
+//
+// Rotation (Fact 3.2, §3.2): for a request with query position m and the
+// segment at start s, the key at in-segment index t sits at s + t and
+//     (R_m q)^T (R_{s+t} k) = (R_{m-s} q)^T (R_t k),
+// so each request's query is rotated once per item by m - s (one table row,
+// the per-document query rotation of §3.2 "Decoding", Eq. 6) and each key by
+// its in-segment index t (table rows 0 .. segment length, shared by every
+// document and hot in L2).  A document-local pool already stores R_t k: its
+// keys are used as loaded.
+//
+// Per 16-key block and wave (the waves take the chunk's blocks round-robin):
+//   S^T[16 keys x 16 cols] = K' Q^T   4 x v_mfma_f32_16x16x32_bf16 per column tile
+//   O^T[128 x 16 cols]    += V^T P^T  8 x v_mfma_f32_16x16x16_bf16 per column tile
+// with up to two column tiles of 16 (member u, head hh) columns.  The K'
+// and V^T operands are loaded and rotated once and used by every column.
+// The four waves merge through LDS and write one fp32 partial (o, m, l) per
+// (member, head); decode_shared_combine_kernel merges each request's partials.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace lazyattn {
+namespace {
+
+constexpr int D = 128;
+constexpr int HALF = 64;
+constexpr int BS = 16;
+constexpr int WAVES = 4;
+constexpr int NT = 2;            // column tiles per item
+constexpr int NCOL = 16 * NT;    // (member, head) columns per item
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ i16x4 as_i16x4(uint2 u) { return __builtin_bit_cast(i16x4, u); }
+
+// Max (or sum) over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four k-groups holding
+// one MFMA column), exchanged in registers with v_permlane16/32_swap.
+__device__ __forceinline__ float column_combine(float x, bool take_max) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  x = take_max ? fmaxf(a, b) : a + b;
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+  return take_max ? fmaxf(a, b) : a + b;
+}
+
+// Rotate 8 pairs (x1[e], x2[e]) with cos/sin c[e], sn[e] and pack the results
+// to bf16: y1 -> lo (first half of the pair), y2 -> hi.
+__device__ __forceinline__ void rotate8(const float (&x1)[8], const float (&x2)[8],
+                                        const float (&c)[8], const float (&sn)[8], uint4& lo,
+                                        uint4& hi) {
+  uint32_t* p1 = reinterpret_cast<uint32_t*>(&lo);
+  uint32_t* p2 = reinterpret_cast<uint32_t*>(&hi);
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    float y1[2], y2[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int e = 2 * e2 + t;
+      y1[t] = x1[e] * c[e] - x2[e] * sn[e];
+      y2[t] = x1[e] * sn[e] + x2[e] * c[e];
+    }
+    p1[e2] = pack_bf16x2(y1[0], y1[1]);
+    p2[e2] = pack_bf16x2(y2[0], y2[1]);
+  }
+}
+
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void widen8(uint4 u, float (&x)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(w[i]);
+    x[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+// MODE 0: position-free pool (keys rotated by their in-segment index);
+// MODE 1: document-local pool (keys stored as R_t k, used as loaded).
+template <int G, int MODE>
+__global__ __launch_bounds__(256, 2) void decode_shared_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
+    const uint16_t* __restrict__ v_pool, const int4* __restrict__ items,
+    const int4* __restrict__ members, const uint64_t* __restrict__ words,
+    const int32_t* __restrict__ q_pos, const float* __restrict__ cs, int Hkv, float qscale,
+    int interleaved, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  static_assert(G >= 1 && G <= 16 && NCOL % G == 0, "group size");
+  constexpr bool RAW_KEYS = MODE == 1;
+  const int Hq = Hkv * G;
+  const int item_idx = blockIdx.x / Hkv;  // consecutive workgroups: same item, kv heads 0..
+  const int g = blockIdx.x - item_idx * Hkv;  // (Hkv = 8: kv head g runs on XCD g)
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;   // MFMA row (key slot) of the A operand / column of the B operand
+  const int gq = lane >> 4;  // MFMA k-group
+
+  __shared__ float mo_lds[WAVES][NCOL][D];
+  __shared__ float mm_lds[WAVES][NCOL];
+  __shared__ float ml_lds[WAVES][NCOL];
+
+  const int4 it = items[item_idx];  // {first word, blocks, first member, members}
+  const int ncols = it.w * G;
+  const int nt = (ncols + 15) >> 4;  // column tiles in use (wave-uniform)
+
+  // ---- queries: column c = 16 ct + n is (member c / G, head c % G), rotated
+  // once by m - s and scaled by scale * log2(e), straight into the B operand.
+  bf16x8 qbv[NT][4];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    const int c = 16 * ct + n;
+    uint4 o[4] = {uint4{0u, 0u, 0u, 0u}, uint4{0u, 0u, 0u, 0u}, uint4{0u, 0u, 0u, 0u},
+                  uint4{0u, 0u, 0u, 0u}};
+    if (c < ncols) {
+      const int4 mb = members[it.z + c / G];
+      const int hh = c % G;
+      int off = q_pos[mb.x] - mb.y;  // m - s
+      float sgn = 1.f;
+      if (off < 0) {  // R_{-x}: the sine changes sign
+        off = -off;
+        sgn = -1.f;
+      }
+      const uint16_t* qrow = q + (static_cast<size_t>(mb.x) * Hq + g * G + hh) * D;
+      const float* row = cs + static_cast<size_t>(off) * D;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int j0 = 32 * s + 8 * gq;  // pairs j0 .. j0 + 7
+        float x1[8], x2[8], cc[8], sn[8];
+        if (interleaved) {  // pair j is (2j, 2j + 1)
+          const uint4 a = *reinterpret_cast<const uint4*>(qrow + 2 * j0);
+          const uint4 b = *reinterpret_cast<const uint4*>(qrow + 2 * j0 + 8);
+          const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            x1[e] = bf16_lo(w[e]);
+            x2[e] = bf16_hi(w[e]);
+          }
+        } else {  // pair j is (j, j + 64)
+          widen8(*reinterpret_cast<const uint4*>(qrow + j0), x1);
+          widen8(*reinterpret_cast<const uint4*>(qrow + j0 + HALF), x2);
+        }
+        load8(row + j0, cc);
+        load8(row + HALF + j0, sn);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x1[e] *= qscale;
+          x2[e] *= qscale;
+          sn[e] *= sgn;
+        }
+        rotate8(x1, x2, cc, sn, o[s], o[s + 2]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qbv[ct][s] = as_bf16x8(o[s]);
+  }
+
+  float mrun[NT], lrun[NT];
+  f32x4 oacc[NT][8];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    mrun[ct] = -INFINITY;
+    lrun[ct] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) oacc[ct][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const uint64_t* wd = words + it.x;
+  const int nblk = it.y;
+  // block words one block ahead (a load at the top of the iteration would put a
+  // memory round trip in front of the K/V loads)
+  uint64_t w_next = wave < nblk ? wd[wave] : 0;
+  for (int b = wave; b < nblk; b += WAVES) {
+    const BlockWord w = unpack_word(w_next);
+    w_next = wd[min(b + WAVES, nblk - 1)];  // past the end: a valid word, unused
+    const size_t tile = static_cast<size_t>(w.block_id) * Hkv + g;
+    const uint16_t* kb = k_pool + tile * (BS * D) + n * D;
+    uint4 kr[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kr[s] = *reinterpret_cast<const uint4*>(kb + 8 * (4 * s + gq));
+    const uint16_t* vb = v_pool + tile * (D * BS) + n * BS + 4 * gq;
+    uint2 vr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vr[j] = *reinterpret_cast<const uint2*>(vb + 16 * j * BS);
+
+    // K' = R_t k with t = this lane's key index in the segment (pos0 field: the
+    // index of slot 0); unused slots read the row of the block's last key.
+    bf16x8 ka[4];
+    if (RAW_KEYS) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ka[s] = as_bf16x8(kr[s]);
+    } else {
+      const int t = w.pos0 + min(n, w.n_valid - 1);
+      const float* row = cs + static_cast<size_t>(t) * D;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int j0 = 32 * s + 8 * gq;
+        float x1[8], x2[8], cc[8], sn[8];
+        widen8(kr[s], x1);
+        widen8(kr[s + 2], x2);
+        load8(row + j0, cc);
+        load8(row + HALF + j0, sn);
+        uint4 lo, hi;
+        rotate8(x1, x2, cc, sn, lo, hi);
+        ka[s] = as_bf16x8(lo);
+        ka[s + 2] = as_bf16x8(hi);
+      }
+    }
+    if (w.n_valid < BS) {
+      // Unused slots may hold anything (even NaN): zero their V entries.
+      const int k0 = 4 * gq;
+      const uint32_t m0 = (k0 + 0 < w.n_valid ? 0x0000FFFFu : 0u) | (k0 + 1 < w.n_valid ? 0xFFFF0000u : 0u);
+      const uint32_t m1 = (k0 + 2 < w.n_valid ? 0x0000FFFFu : 0u) | (k0 + 3 < w.n_valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        vr[j].x &= m0;
+        vr[j].y &= m1;
+      }
+    }
+
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      if (ct >= nt) break;  // wave-uniform
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qbv[ct][s], sacc, 0, 0, 0);
+      // sacc[i] = score(key slot 4 gq + i, column n) in log2 units
+      if (w.n_valid < BS) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * gq + i >= w.n_valid) sacc[i] = -INFINITY;
+      }
+      float bm = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
+      bm = column_combine(bm, true);
+      const float mnew = fmaxf(mrun[ct], bm);
+      const float alpha = __builtin_amdgcn_exp2f(mrun[ct] - mnew);
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sacc[i] - mnew);
+      lrun[ct] = lrun[ct] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+      mrun[ct] = mnew;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) oacc[ct][j] *= alpha;
+      uint2 pb;
+      pb.x = pack_bf16x2(p[0], p[1]);
+      pb.y = pack_bf16x2(p[2], p[3]);
+      const i16x4 pbv = as_i16x4(pb);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        oacc[ct][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(vr[j]), pbv, oacc[ct][j],
+                                                                 0, 0, 0);
+    }
+  }
+
+  // Wave state -> LDS: lane (n, gq) holds O^T[16 j + 4 gq + i][column 16 ct + n].
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    const float l = column_combine(lrun[ct], false);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mo_lds[wave][16 * ct + n][16 * j + 4 * gq + i] = oacc[ct][j][i];
+    if (gq == 0) {
+      mm_lds[wave][16 * ct + n] = mrun[ct];
+      ml_lds[wave][16 * ct + n] = l;
+    }
+  }
+  __syncthreads();
+
+  // Merge the four waves; one fp32 partial per (member, head).
+  for (int idx = threadIdx.x; idx < ncols * D; idx += 256) {
+    const int c = idx / D;
+    const int d = idx - c * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < WAVES; ++wv) M = fmaxf(M, mm_lds[wv][c]);
+    float O = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int wv = 0; wv < WAVES; ++wv) {
+        const float f = __builtin_amdgcn_exp2f(mm_lds[wv][c] - M);
+        O += f * mo_lds[wv][c][d];
+        L += f * ml_lds[wv][c];
+      }
+    }
+    const int slot = members[it.z + c / G].z;
+    const size_t ph = static_cast<size_t>(slot) * Hq + g * G + c % G;
+    part_o[ph * D + d] = O;
+    if (d == 0) {
+      part_ml[ph * 2] = M;
+      part_ml[ph * 2 + 1] = L;
+    }
+  }
+}
+
+// Merge each request's partials: one wave per (request, query head).
+__global__ __launch_bounds__(64) void decode_shared_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ req_part_start, int Hq, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  const int rh = blockIdx.x;
+  const int r = rh / Hq;
+  const int h = rh - r * Hq;
+  const int lane = threadIdx.x;
+  const int s0 = req_part_start[r], s1 = req_part_start[r + 1];
+  float M = -INFINITY;
+  for (int s = s0; s < s1; ++s) M = fmaxf(M, part_ml[(static_cast<size_t>(s) * Hq + h) * 2]);
+  float o0 = 0.f, o1 = 0.f, L = 0.f;
+  if (M != -INFINITY) {
+    for (int s = s0; s < s1; ++s) {
+      const size_t ph = static_cast<size_t>(s) * Hq + h;
+      const float ms = part_ml[ph * 2];
+      if (ms == -INFINITY) continue;
+      const float f = __builtin_amdgcn_exp2f(ms - M);
+      const float2 o = *reinterpret_cast<const float2*>(part_o + ph * D + 2 * lane);
+      o0 += f * o.x;
+      o1 += f * o.y;
+      L += f * part_ml[ph * 2 + 1];
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  *reinterpret_cast<uint32_t*>(out + static_cast<size_t>(rh) * D + 2 * lane) =
+      pack_bf16x2(o0 * inv, o1 * inv);
+  if (lse != nullptr && lane == 0) lse[rh] = L > 0.f ? (M + __log2f(L)) * LN2 : -INFINITY;
+}
+
+template <int G, int MODE>
+hipError_t launch_g(const AttnArgs& a, const SharedPlanView& v, void* ws, hipStream_t stream) {
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = part_o + static_cast<size_t>(v.n_partials) * a.num_q_heads * D;
+  hipLaunchKernelGGL((decode_shared_kernel<G, MODE>), dim3(v.n_items * a.num_kv_heads), dim3(256),
+                     0, stream, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
+                     v.items, v.members, v.words, a.q_pos, a.cos_sin, a.num_kv_heads,
+                     a.scale * LOG2E, a.pos_encoding == 1 ? 1 : 0, part_o, part_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_shared_combine_kernel, dim3(a.batch * a.num_q_heads), dim3(64), 0,
+                     stream, part_o, part_ml, v.req_part_start, a.num_q_heads,
+                     static_cast<uint16_t*>(a.out), a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t decode_shared_workspace_bytes(int n_partials, int num_q_heads) {
+  return static_cast<size_t>(n_partials) * num_q_heads * (D + 2) * sizeof(float);
+}
+
+hipError_t launch_decode_shared_bf16(const AttnArgs& a, const SharedPlanView& v, void* workspace,
+                                     hipStream_t stream) {
+  const int mode = a.pool_mode == 1 ? 1 : 0;
+#define LAZYATTN_SHARED_G(GG)                                                       \
+  case GG:                                                                          \
+    return mode == 0 ? launch_g<GG, 0>(a, v, workspace, stream)                     \
+                     : launch_g<GG, 1>(a, v, workspace, stream);
+  switch (a.num_q_heads / a.num_kv_heads) {
+    LAZYATTN_SHARED_G(1)
+    LAZYATTN_SHARED_G(2)
+    LAZYATTN_SHARED_G(4)
+    LAZYATTN_SHARED_G(8)
+    LAZYATTN_SHARED_G(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef LAZYATTN_SHARED_G
+}
+
+}  // namespace lazyattn

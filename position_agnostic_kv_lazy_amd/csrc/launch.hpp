@@ -54,6 +54,23 @@ hipError_t launch_decode_bf16(const AttnArgs& a, const DecodeSplit& s, void* wor
 // (LA_DECODE_NOALLOC_SCRATCH_BYTES bytes, resolved once per device).
 hipError_t decode_scratch_ptr(void** out);
 
+// Device views into a shared-segment decode plan blob (layout in lazy_attn.h).
+struct SharedPlanView {
+  const int4* items;             // {first word, blocks, first member, members}
+  const int4* members;           // {request, segment start, partial slot, 0}
+  const int32_t* req_part_start; // [batch + 1]
+  const uint64_t* words;         // per chunk block: id | slot-0 index << 32 | (n_valid-1) << 56
+  int n_items;
+  int n_partials;
+};
+
+// Bytes of fp32 partials (o, m, l) for n_partials slots of all query heads.
+size_t decode_shared_workspace_bytes(int n_partials, int num_q_heads);
+
+// bf16 shared-segment decode + the per-request merge of its partials.
+hipError_t launch_decode_shared_bf16(const AttnArgs& a, const SharedPlanView& v, void* workspace,
+                                     hipStream_t stream);
+
 // bf16 MFMA prefill.
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
 

@@ -11,6 +11,7 @@
 #include <new>
 #include <string>
 #include <thread>
+#include <unordered_map>
 #include <vector>
 
 #include "lazy_attn.h"
@@ -158,6 +159,80 @@ la_status fetch(const T* src, size_t n, std::vector<T>& dst) {
   hipError_t e = hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy (validate_table)");
   return LA_OK;
+}
+
+// Segment-list checks shared by lazy_attn_pack_segments and the shared-decode
+// planner: every segment non-empty, inside [0, max_pos), with exactly the block
+// count its length needs, block ids inside the pool, every request non-empty.
+la_status check_segments(const la_params* p, int32_t batch, const int64_t* req_seg_start,
+                         const int64_t* seg_start, const int64_t* seg_len,
+                         const int64_t* seg_blk_start, const int64_t* seg_blocks) {
+  const int64_t BS = p->block_size;
+  if (req_seg_start[0] != 0) return fail(LA_ERR_INVALID_ARG, "req_seg_start[0] must be 0");
+  for (int r = 0; r < batch; ++r) {
+    const int64_t s0 = req_seg_start[r], s1 = req_seg_start[r + 1];
+    if (s1 < s0) return fail(LA_ERR_INVALID_ARG, "req_seg_start decreases at request %d", r);
+    if (s1 == s0) return fail(LA_ERR_INVALID_ARG, "request %d has no keys", r);
+    for (int64_t s = s0; s < s1; ++s) {
+      const int64_t n = seg_len[s], start = seg_start[s];
+      if (n < 1) return fail(LA_ERR_INVALID_ARG, "segment %lld has %lld tokens", (long long)s, (long long)n);
+      if (start < 0 || start + n - 1 >= p->max_pos)
+        return fail(LA_ERR_INVALID_ARG,
+                    "segment %lld covers positions [%lld, %lld], outside [0, max_pos=%lld)",
+                    (long long)s, (long long)start, (long long)(start + n - 1),
+                    (long long)p->max_pos);
+      const int64_t nb = (n + BS - 1) / BS;
+      if (seg_blk_start[s + 1] - seg_blk_start[s] != nb)
+        return fail(LA_ERR_INVALID_ARG, "segment %lld of %lld tokens lists %lld blocks, needs %lld",
+                    (long long)s, (long long)n, (long long)(seg_blk_start[s + 1] - seg_blk_start[s]),
+                    (long long)nb);
+      for (int64_t k = 0; k < nb; ++k) {
+        const int64_t id = seg_blocks[seg_blk_start[s] + k];
+        if (id < 0 || id >= p->num_blocks)
+          return fail(LA_ERR_INVALID_ARG, "block id %lld outside [0, num_blocks=%lld)",
+                      (long long)id, (long long)p->num_blocks);
+      }
+    }
+  }
+  return LA_OK;
+}
+
+// Identity of a segment for the shared decode: its length and block list.
+struct SegKey {
+  const int64_t* blocks;
+  int64_t nb;
+  int64_t len;
+  bool operator==(const SegKey& o) const {
+    return len == o.len && nb == o.nb && std::equal(blocks, blocks + nb, o.blocks);
+  }
+};
+struct SegKeyHash {
+  size_t operator()(const SegKey& k) const {
+    uint64_t h = 1469598103934665603ull ^ static_cast<uint64_t>(k.len);
+    for (int64_t i = 0; i < k.nb; ++i) {
+      h ^= static_cast<uint64_t>(k.blocks[i]);
+      h *= 1099511628211ull;
+    }
+    return static_cast<size_t>(h);
+  }
+};
+
+constexpr int kSharedColumns = 32;  // (member, head) columns per work item
+constexpr int kSharedDefaultChunk = 32;
+
+int64_t align16(int64_t x) { return (x + 15) & ~int64_t{15}; }
+
+// Byte offsets of the plan blob's sections (layout in lazy_attn.h).
+struct PlanOffsets {
+  int64_t members, req_part_start, words, end;
+};
+PlanOffsets plan_offsets(int64_t n_items, int64_t n_members, int64_t batch, int64_t n_words) {
+  PlanOffsets o;
+  o.members = 16 * n_items;
+  o.req_part_start = o.members + 16 * n_members;
+  o.words = o.req_part_start + align16(4 * (batch + 1));
+  o.end = o.words + 8 * n_words;
+  return o;
 }
 
 }  // namespace
@@ -574,6 +649,192 @@ LA_API la_status lazy_attn_decode_noalloc(const la_params* p, const void* q, con
     return ok();
   } catch (...) {
     return fail(LA_ERR_HIP, "unexpected exception in lazy_attn_decode_noalloc");
+  }
+}
+
+LA_API la_status lazy_attn_plan_shared_decode(
+    const la_params* p, int32_t batch, const int64_t* req_seg_start, const int64_t* seg_start,
+    const int64_t* seg_len, const uint8_t* seg_is_new, const int64_t* seg_blk_start,
+    const int64_t* seg_blocks, int32_t max_item_blocks, la_shared_plan_info* info, void* plan,
+    int64_t plan_capacity) {
+  try {
+    la_status st = check_params(p);
+    if (st != LA_OK) return st;
+    if (p->dtype != LA_BF16)
+      return fail(LA_ERR_UNSUPPORTED, "the shared-segment decode is built for bf16 only");
+    if (p->pos_encoding == LA_ALIBI)
+      return fail(LA_ERR_UNSUPPORTED, "the shared-segment decode does not support ALiBi");
+    if (batch < 1) return fail(LA_ERR_INVALID_ARG, "batch must be >= 1");
+    if (!req_seg_start || !seg_start || !seg_len || !seg_is_new || !seg_blk_start || !seg_blocks ||
+        !info)
+      return fail(LA_ERR_INVALID_ARG, "NULL array passed to lazy_attn_plan_shared_decode");
+    if (max_item_blocks < 0 || max_item_blocks > (1 << 20))
+      return fail(LA_ERR_INVALID_ARG, "max_item_blocks %d outside [0, 2^20]", max_item_blocks);
+    if ((st = check_segments(p, batch, req_seg_start, seg_start, seg_len, seg_blk_start,
+                             seg_blocks)) != LA_OK)
+      return st;
+    const int64_t BS = p->block_size;
+    const int G = p->num_q_heads / p->num_kv_heads;
+    const int64_t C = kSharedColumns / G;  // members per item
+    const int64_t MIB = max_item_blocks > 0 ? max_item_blocks : kSharedDefaultChunk;
+
+    // Group identical segments; every (request, segment chunk) gets one
+    // partial slot, numbered request by request (the merge reads a range).
+    struct Member {
+      int32_t r;
+      int64_t start;
+      int64_t first_slot;
+    };
+    struct Group {
+      int64_t seg;  // a representative segment: its length and blocks
+      std::vector<Member> members;
+    };
+    std::unordered_map<SegKey, int64_t, SegKeyHash> index;
+    std::vector<Group> groups;
+    std::vector<int32_t> req_part_start(static_cast<size_t>(batch) + 1);
+    int64_t slot = 0;
+    for (int r = 0; r < batch; ++r) {
+      req_part_start[r] = static_cast<int32_t>(slot);
+      for (int64_t s = req_seg_start[r]; s < req_seg_start[r + 1]; ++s) {
+        const int64_t nb = (seg_len[s] + BS - 1) / BS;
+        const SegKey key{seg_blocks + seg_blk_start[s], nb, seg_len[s]};
+        auto it = index.find(key);
+        int64_t gi;
+        if (it == index.end()) {
+          gi = static_cast<int64_t>(groups.size());
+          index.emplace(key, gi);
+          groups.push_back(Group{s, {}});
+        } else {
+          gi = it->second;
+        }
+        groups[gi].members.push_back(Member{r, seg_start[s], slot});
+        slot += (nb + MIB - 1) / MIB;
+        if (slot > INT32_MAX / 2) return fail(LA_ERR_INVALID_ARG, "too many segment chunks");
+      }
+    }
+    req_part_start[batch] = static_cast<int32_t>(slot);
+
+    // Items: per distinct segment, per chunk, runs of at most C members.
+    struct Item {
+      int32_t word0, nblk, mem0, nmem;
+    };
+    std::vector<Item> items;
+    std::vector<int32_t> mem;  // 4 per member
+    std::vector<uint64_t> words;
+    for (const Group& gr : groups) {
+      const int64_t len = seg_len[gr.seg];
+      const int64_t nb = (len + BS - 1) / BS;
+      const int64_t* blocks = seg_blocks + seg_blk_start[gr.seg];
+      for (int64_t c0 = 0, chunk = 0; c0 < nb; c0 += MIB, ++chunk) {
+        const int64_t c1 = std::min(nb, c0 + MIB);
+        const int64_t w0 = static_cast<int64_t>(words.size());
+        for (int64_t k = c0; k < c1; ++k) {
+          const int nv = static_cast<int>(k + 1 < nb ? BS : len - k * BS);
+          words.push_back(pack_word(blocks[k], k * BS, nv, false));
+        }
+        for (size_t m0 = 0; m0 < gr.members.size(); m0 += static_cast<size_t>(C)) {
+          const size_t m1 = std::min(gr.members.size(), m0 + static_cast<size_t>(C));
+          items.push_back(Item{static_cast<int32_t>(w0), static_cast<int32_t>(c1 - c0),
+                               static_cast<int32_t>(mem.size() / 4),
+                               static_cast<int32_t>(m1 - m0)});
+          for (size_t m = m0; m < m1; ++m) {
+            const Member& mb = gr.members[m];
+            mem.push_back(mb.r);
+            mem.push_back(static_cast<int32_t>(mb.start));
+            mem.push_back(static_cast<int32_t>(mb.first_slot + chunk));
+            mem.push_back(0);
+          }
+        }
+      }
+      if (words.size() > static_cast<size_t>(INT32_MAX / 2) ||
+          items.size() * static_cast<size_t>(p->num_kv_heads) > static_cast<size_t>(INT32_MAX / 2))
+        return fail(LA_ERR_INVALID_ARG, "shared-decode plan too large");
+    }
+    // Longest chunks first (a short tail of small items), stable so the items
+    // of one chunk stay adjacent and run together (their K/V tiles meet in L2).
+    std::stable_sort(items.begin(), items.end(),
+                     [](const Item& a, const Item& b) { return a.nblk > b.nblk; });
+
+    const int64_t n_items = static_cast<int64_t>(items.size());
+    const int64_t n_members = static_cast<int64_t>(mem.size() / 4);
+    const int64_t n_words = static_cast<int64_t>(words.size());
+    const PlanOffsets off = plan_offsets(n_items, n_members, batch, n_words);
+    info->batch = batch;
+    info->n_items = static_cast<int32_t>(n_items);
+    info->n_members = static_cast<int32_t>(n_members);
+    info->n_words = static_cast<int32_t>(n_words);
+    info->members_per_item = static_cast<int32_t>(C);
+    info->max_item_blocks = static_cast<int32_t>(MIB);
+    info->plan_bytes = off.end;
+    info->workspace_bytes = static_cast<int64_t>(
+        lazyattn::decode_shared_workspace_bytes(static_cast<int>(n_members), p->num_q_heads));
+    if (plan == nullptr) return ok();
+    if (plan_capacity < off.end)
+      return fail(LA_ERR_INVALID_ARG, "plan capacity %lld below the %lld bytes needed",
+                  (long long)plan_capacity, (long long)off.end);
+    char* base = static_cast<char*>(plan);
+    std::memset(base, 0, static_cast<size_t>(off.end));
+    std::memcpy(base, items.data(), items.size() * sizeof(Item));
+    std::memcpy(base + off.members, mem.data(), mem.size() * sizeof(int32_t));
+    std::memcpy(base + off.req_part_start, req_part_start.data(),
+                req_part_start.size() * sizeof(int32_t));
+    std::memcpy(base + off.words, words.data(), words.size() * sizeof(uint64_t));
+    return ok();
+  } catch (const std::bad_alloc&) {
+    return fail(LA_ERR_INVALID_ARG, "out of host memory in lazy_attn_plan_shared_decode");
+  } catch (...) {
+    return fail(LA_ERR_INVALID_ARG, "unexpected exception in lazy_attn_plan_shared_decode");
+  }
+}
+
+LA_API la_status lazy_attn_decode_shared(const la_params* p, const la_shared_plan_info* info,
+                                         const void* plan, const void* q, const void* k_pool,
+                                         const void* v_pool, const int32_t* q_pos,
+                                         const float* cos_sin, int32_t batch, void* out,
+                                         float* lse, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  try {
+    la_status st = check_params(p);
+    if (st != LA_OK) return st;
+    if (p->dtype != LA_BF16)
+      return fail(LA_ERR_UNSUPPORTED, "the shared-segment decode is built for bf16 only");
+    if (p->pos_encoding == LA_ALIBI)
+      return fail(LA_ERR_UNSUPPORTED, "the shared-segment decode does not support ALiBi");
+    if (!info || !plan || !q || !k_pool || !v_pool || !q_pos || !cos_sin || !out)
+      return fail(LA_ERR_INVALID_ARG, "NULL pointer passed to lazy_attn_decode_shared");
+    if (batch < 1 || info->batch != batch)
+      return fail(LA_ERR_INVALID_ARG, "batch %d does not match the plan's %d", batch,
+                  info->batch);
+    const int G = p->num_q_heads / p->num_kv_heads;
+    if (info->n_items < 1 || info->n_members < 1 || info->n_words < 1 ||
+        info->members_per_item != kSharedColumns / G)
+      return fail(LA_ERR_INVALID_ARG, "plan sizes do not fit these params");
+    const PlanOffsets off = plan_offsets(info->n_items, info->n_members, batch, info->n_words);
+    if (off.end != info->plan_bytes)
+      return fail(LA_ERR_INVALID_ARG, "plan_bytes does not match the plan's counts");
+    if (reinterpret_cast<uintptr_t>(plan) % 16 != 0)
+      return fail(LA_ERR_INVALID_ARG, "plan must be 16-byte aligned");
+    const size_t need = lazyattn::decode_shared_workspace_bytes(info->n_members, p->num_q_heads);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(LA_ERR_WORKSPACE_TOO_SMALL, "shared decode needs %zu workspace bytes, got %zu",
+                  need, workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+    const char* base = static_cast<const char*>(plan);
+    lazyattn::SharedPlanView v;
+    v.items = reinterpret_cast<const int4*>(base);
+    v.members = reinterpret_cast<const int4*>(base + off.members);
+    v.req_part_start = reinterpret_cast<const int32_t*>(base + off.req_part_start);
+    v.words = reinterpret_cast<const uint64_t*>(base + off.words);
+    v.n_items = info->n_items;
+    v.n_partials = info->n_members;
+    const lazyattn::AttnArgs a = make_args(p, q, k_pool, v_pool, nullptr, nullptr, nullptr, q_pos,
+                                           cos_sin, batch, 1, 0, out, lse);
+    clear_stale_hip_error();
+    const hipError_t e =
+        lazyattn::launch_decode_shared_bf16(a, v, workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "lazy_attn_decode_shared launch");
+    return ok();
+  } catch (...) {
+    return fail(LA_ERR_HIP, "unexpected exception in lazy_attn_decode_shared");
   }
 }
 

@@ -66,9 +66,15 @@ class DeviceBatch:
     max_q: int
     host_words: np.ndarray
     host_rbs: np.ndarray
+    plan: Optional[torch.Tensor] = None       # shared-segment decode plan (device)
+    plan_info: Optional[B.la_shared_plan_info] = None
 
     def run(self, stream=None):
-        if self.kind == "decode":
+        if self.kind == "decode" and self.plan is not None:
+            B.lazy_attn_decode_shared(self.params, self.plan_info, self.plan, self.q, self.k_pool,
+                                      self.v_pool, self.q_pos, self.cos_sin, self.batch, self.out,
+                                      self.lse, self.workspace, stream)
+        elif self.kind == "decode":
             B.lazy_attn_decode(self.params, self.q, self.k_pool, self.v_pool, self.words,
                                self.req_blk_start, self.q_pos, self.cos_sin, self.batch,
                                self.max_blocks, self.out, self.lse, self.workspace, stream)
@@ -150,12 +156,15 @@ def store_pool(w, k_tok: np.ndarray, v_tok: np.ndarray, slots: np.ndarray,
 def prepare(w, k_dev: torch.Tensor, v_dev: torch.Tensor, device="cuda", split_blocks: int = 0,
             target_workgroups: int = 0, max_pos: Optional[int] = None,
             pool_mode="position_free", pos_encoding="rope_half",
-            table: Optional[np.ndarray] = None) -> DeviceBatch:
+            table: Optional[np.ndarray] = None, shared: bool = False,
+            max_item_blocks: int = 0) -> DeviceBatch:
     """Pack and upload everything lazy_attn_decode/prefill need for batch w.
 
     table overrides the position table handed to the kernels: by default the
     RoPE cos/sin rows (lazy_attn_rope_table) or, for ALiBi, the standard
-    slopes (lazy_attn_alibi_slopes).
+    slopes (lazy_attn_alibi_slopes).  shared=True (decode) builds a
+    shared-segment plan (lazy_attn_plan_shared_decode) and runs
+    lazy_attn_decode_shared instead of lazy_attn_decode.
     """
     rows = int(max_pos) if max_pos is not None else int(w.table_rows())
     params = params_for(w, int(k_dev.shape[0]), rows, split_blocks, target_workgroups, pool_mode,
@@ -175,7 +184,12 @@ def prepare(w, k_dev: torch.Tensor, v_dev: torch.Tensor, device="cuda", split_bl
         cu_q = torch.from_numpy(cu).to(device)
         max_q = int(np.max(np.diff(cu)))
     ws = None
-    if w.kind == "decode":
+    plan = info = None
+    if w.kind == "decode" and shared:
+        info, blob = B.lazy_attn_plan_shared_decode(params, w.requests, max_item_blocks)
+        plan = torch.from_numpy(blob).to(device)
+        ws = torch.empty(int(info.workspace_bytes), dtype=torch.uint8, device=device)
+    elif w.kind == "decode":
         nbytes = B.lazy_attn_decode_workspace_size(params, w.batch, maxb)
         if nbytes:
             ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -185,4 +199,5 @@ def prepare(w, k_dev: torch.Tensor, v_dev: torch.Tensor, device="cuda", split_bl
         req_blk_start=torch.from_numpy(rbs).to(device), q_pos=q_pos, cu_q=cu_q,
         cos_sin=torch.from_numpy(np.ascontiguousarray(table, np.float32)).to(device), out=out,
         lse=lse, workspace=ws,
-        batch=w.batch, max_blocks=maxb, max_q=max_q, host_words=words, host_rbs=rbs)
+        batch=w.batch, max_blocks=maxb, max_q=max_q, host_words=words, host_rbs=rbs,
+        plan=plan, plan_info=info)
