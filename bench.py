@@ -47,10 +47,13 @@ WARM_S = 0.25                # minimum warm-up (seconds of launches) for every l
 BF16_MAX_ABS, BF16_REL_L2 = 2e-2, 5e-3
 KERNEL_SRC = {
     "decode": os.path.join(ROOT, "position_agnostic_kv_lazy_amd", "csrc", "decode_bf16.hip"),
+    "decode_shared": os.path.join(ROOT, "position_agnostic_kv_lazy_amd", "csrc",
+                                  "decode_shared_bf16.hip"),
     "prefill": os.path.join(ROOT, "position_agnostic_kv_lazy_amd", "csrc", "prefill_bf16.hip"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-LEGS = ("headline", "ablation", "prefill", "long_decode", "mixed", "no_sharing", "references")
+LEGS = ("headline", "other_decode", "ablation", "prefill", "long_decode", "mixed", "no_sharing",
+        "references")
 
 
 def log(msg):
@@ -214,9 +217,14 @@ def _ms(x):
     return round(x, 5)
 
 
-def run_decode_workload(w, k, v, stream, steps, warmup, split_blocks=0, cold=True):
+MAX_ITEM_BLOCKS = 0  # shared-decode chunk length (0: the library default); set by --max-item-blocks
+
+
+def run_decode_workload(w, k, v, stream, steps, warmup, split_blocks=0, cold=True, shared=False):
+    """Time one decode workload: lazy_attn_decode_shared (shared=True) or lazy_attn_decode."""
     from position_agnostic_kv_lazy_amd.prepare import prepare
-    db = prepare(w, k, v, split_blocks=split_blocks)
+    db = prepare(w, k, v, split_blocks=split_blocks, shared=shared,
+                 max_item_blocks=MAX_ITEM_BLOCKS)
     run = lambda: db.run(stream)  # noqa: E731
     t = time_launches(run, steps, warmup, stream)
     nbytes = w.logical_kv_bytes()
@@ -229,8 +237,12 @@ def run_decode_workload(w, k, v, stream, steps, warmup, split_blocks=0, cold=Tru
         "event_ms_p10": t["p10"], "event_ms_p90": t["p90"],
         "gbs_logical": nbytes / (t["mean"] * 1e-3) / 1e9,
         "workspace_bytes": 0 if db.workspace is None else int(db.workspace.numel()),
+        "decode_kernel": "shared" if shared else "per_request",
         "_db": db,
     }
+    if shared:
+        res["plan"] = {"items": db.plan_info.n_items, "partials": db.plan_info.n_members,
+                       "distinct_chunk_blocks": db.plan_info.n_words}
     if cold:
         read_sweep, write_fill = make_flushers()
         n = max(5, steps // 2)
@@ -271,8 +283,12 @@ def roofline_hbm(res, kind, workload, split):
     """Decode HBM roofline on the bytes HBM delivers per launch (rocprofv3
     counters, same kernel source) over the launch time by HIP events."""
     ms = res["event_ms_mean"]
+    if res.get("decode_kernel") == "shared":
+        kind = "decode_shared"
+        kern = "decode_shared_kernel + decode_shared_combine_kernel"
+    else:
+        kern = "decode_bf16_kernel + decode_combine_kernel" if split else "decode_bf16_kernel"
     traffic = traffic_for(kind, workload)
-    kern = "decode_bf16_kernel + decode_combine_kernel" if split else "decode_bf16_kernel"
     per_launch = {"algorithmic_bytes": res["logical_kv_bytes"],
                   "unique_bytes": res["unique_kv_bytes"],
                   "logical_gbs": round(res["logical_kv_bytes"] / (ms * 1e-3) / 1e9, 1),
@@ -304,7 +320,7 @@ def _clean(res):
 
 
 # ---------------------------------------------------------------- extra legs
-def _extra_no_sharing(stream, steps, warmup):
+def _extra_no_sharing(stream, steps, warmup, shared):
     """Control for the shared-document mix: configuration 2's shapes with every
     request reading its own documents, so logical bytes = unique bytes = what
     DRAM must deliver."""
@@ -314,7 +330,7 @@ def _extra_no_sharing(stream, steps, warmup):
         log("no-sharing control (64 requests x 10 private documents)")
         w = make_no_sharing_decode()
         k, v = upload_pool(w.k_pool, w.v_pool)
-        res = run_decode_workload(w, k, v, stream, steps, warmup)
+        res = run_decode_workload(w, k, v, stream, steps, warmup, shared=shared)
         out = _clean(res)
         out["frac_of_hbm_peak"] = round(res["gbs_logical"] / HBM_PEAK_GBS, 4)
         out["cold_frac_of_hbm_peak"] = round(res["cold_gbs_logical"] / HBM_PEAK_GBS, 4)
@@ -400,14 +416,14 @@ def _extra_prefill(w3, stream, steps, warmup, oracle):
         return {"llama3_8b_prefill": {"error": repr(e)}}
 
 
-def _extra_long_decode(stream, steps, warmup):
+def _extra_long_decode(stream, steps, warmup, shared):
     from position_agnostic_kv_lazy_amd.prepare import upload_pool
     from workloads import make_config
     try:
         log("long-context decode (16 requests x 64K keys)")
         w4 = make_config(4)
         k4, v4 = upload_pool(w4.k_pool, w4.v_pool)
-        r4 = run_decode_workload(w4, k4, v4, stream, steps, warmup)
+        r4 = run_decode_workload(w4, k4, v4, stream, steps, warmup, shared=shared)
         out = _clean(r4)
         out["roofline"] = roofline_hbm(r4, "decode", w4.name, r4["workspace_bytes"] > 0)
         return {w4.name: out}
@@ -415,7 +431,7 @@ def _extra_long_decode(stream, steps, warmup):
         return {"long_decode": {"error": repr(e)}}
 
 
-def _extra_mixed(stream, steps, warmup):
+def _extra_mixed(stream, steps, warmup, shared):
     """Config 5: one decode launch and one prefill launch on one shared pool."""
     import torch
 
@@ -425,7 +441,7 @@ def _extra_mixed(stream, steps, warmup):
         log("mixed step: 128 decode + 4 prefill requests on one pool")
         m5 = make_config(5)
         k5, v5 = upload_pool(m5.prefill.k_pool, m5.prefill.v_pool)
-        dd = prepare(m5.decode, k5, v5)
+        dd = prepare(m5.decode, k5, v5, shared=shared, max_item_blocks=MAX_ITEM_BLOCKS)
         dp = prepare(m5.prefill, k5, v5)
         s2 = torch.cuda.Stream()
 
@@ -457,7 +473,7 @@ def _extra_mixed(stream, steps, warmup):
             "decode_gbs_logical": round(nb / (dm["mean"] * 1e-3) / 1e9, 1),
             "prefill_tflops": round(fl / (fm["mean"] * 1e-3) / 1e12, 1),
             "decode_logical_kv_bytes": nb, "decode_unique_kv_bytes": m5.decode.unique_kv_bytes(),
-            "prefill_flops": fl,
+            "prefill_flops": fl, "decode_kernel": "shared" if shared else "per_request",
             "warmup_launches": {"pair_two_streams": p2["warmup_launches"],
                                 "pair_serial": p1["warmup_launches"],
                                 "decode": dm["warmup_launches"],
@@ -508,8 +524,8 @@ def _extra_rotation_ablation(w, k, v, stream, steps, warmup, pf_out):
         return lambda: B.lazy_attn_store_kv(params, kt, vt, len(dst_np), dst, pos, cs, kd, vd,
                                             stream)
 
-    def decode(wx, kd, vd):
-        db = prepare(wx, kd, vd, pool_mode="doc_local", max_pos=rows)
+    def decode(wx, kd, vd, shared=False):
+        db = prepare(wx, kd, vd, pool_mode="doc_local", max_pos=rows, shared=shared)
         t = time_launches(lambda: db.run(stream), steps, warmup, stream)
         torch.cuda.synchronize()
         diff = float((db.out.view(torch.bfloat16).float() - pos_free).abs().max())
@@ -530,6 +546,12 @@ def _extra_rotation_ablation(w, k, v, stream, steps, warmup, pf_out):
         "decode_warmup_launches": td["warmup_launches"],
         "write_tokens": int(len(slots)), "write_event_ms_mean": _ms(tw["mean"]),
         "write_gbs": round(moved / (tw["mean"] * 1e-3) / 1e9, 1),
+        "max_abs_diff_vs_position_free": diff}
+    ts, diff = decode(w, kd, vd, shared=True)
+    res["doc_local_shared_decode"] = {
+        "decode_event_ms_mean": _ms(ts["mean"]),
+        "decode_gbs_logical": round(nbytes / (ts["mean"] * 1e-3) / 1e9, 1),
+        "decode_warmup_launches": ts["warmup_launches"],
         "max_abs_diff_vs_position_free": diff}
     del kt, vt, kd, vd
     torch.cuda.empty_cache()
@@ -564,6 +586,15 @@ def _extra_rotation_ablation(w, k, v, stream, steps, warmup, pf_out):
     res["alibi"] = {"decode_event_ms_mean": _ms(ta["mean"]),
                     "decode_gbs_logical": round(nbytes / (ta["mean"] * 1e-3) / 1e9, 1),
                     "decode_warmup_launches": ta["warmup_launches"]}
+    # the position-free pool under the per-request kernel, timed like the rows above
+    db = prepare(w, k, v, max_pos=rows)
+    tp = time_launches(lambda: db.run(stream), steps, warmup, stream)
+    res["position_free"] = {"decode_event_ms_mean": _ms(tp["mean"]),
+                            "decode_gbs_logical": round(nbytes / (tp["mean"] * 1e-3) / 1e9, 1),
+                            "decode_warmup_launches": tp["warmup_launches"]}
+    res["note"] = ("doc_local, materialised, alibi and position_free run the per-request kernel "
+                   "(lazy_attn_decode); doc_local_shared runs the shared-segment kernel over the "
+                   "document-local pool")
     return res
 
 
@@ -580,9 +611,16 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline leg only")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--split-blocks", type=int, default=0)
+    ap.add_argument("--decode", choices=["shared", "per_request"], default="shared",
+                    help="decode kernel: lazy_attn_decode_shared (each shared segment read once "
+                         "per launch) or lazy_attn_decode (one split per request)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB device copies (to scale PMC byte counters)")
+    ap.add_argument("--max-item-blocks", type=int, default=0,
+                    help="shared decode: blocks per work item (0 = library default)")
     args = ap.parse_args()
+    global MAX_ITEM_BLOCKS
+    MAX_ITEM_BLOCKS = args.max_item_blocks
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -636,16 +674,32 @@ def main():
         log("headline leg skipped (--legs): value and roofline are null")
     elif w.kind == "decode":
         k, v = upload_pool(w.k_pool, w.v_pool)
-        log("timing headline decode")
-        main_res = run_decode_workload(w, k, v, stream, args.steps, args.warmup, args.split_blocks)
+        shared = args.decode == "shared"
+        log(f"timing headline decode ({args.decode})")
+        main_res = run_decode_workload(w, k, v, stream, args.steps, args.warmup, args.split_blocks,
+                                       shared=shared)
         torch.cuda.synchronize()
         head_out = main_res["_db"].out_f32()
+        if "other_decode" in legs:
+            other = "per_request" if shared else "shared"
+            log(f"the other decode kernel ({other}) on the headline batch")
+            try:
+                o = run_decode_workload(w, k, v, stream, steps2, args.warmup, args.split_blocks,
+                                        shared=not shared)
+                torch.cuda.synchronize()
+                diff = float(np.max(np.abs(o["_db"].out_f32() - head_out)))
+                oc = _clean(o)
+                oc["roofline"] = roofline_hbm(o, "decode", wl_name, o["workspace_bytes"] > 0)
+                oc["max_abs_diff_vs_headline_kernel"] = diff
+                extra[f"{wl_name}_{other}_decode"] = oc
+                del o
+            except Exception as e:  # reported, never hidden
+                extra[f"{wl_name}_{other}_decode"] = {"error": repr(e)}
         if "ablation" in legs:
             log("rotation ablation: doc-local pool, materialised copies, ALiBi")
             try:
                 ablation = _extra_rotation_ablation(w, k, v, stream, steps2, args.warmup,
                                                     main_res["_db"].out.view(torch.bfloat16))
-                ablation["position_free_decode_event_ms_mean"] = _ms(main_res["event_ms_mean"])
             except Exception as e:  # reported, never hidden
                 ablation = {"error": repr(e)}
             torch.cuda.empty_cache()
@@ -674,13 +728,13 @@ def main():
         extra.update(_extra_prefill(w3, stream, steps2, args.warmup, oracle))
         torch.cuda.empty_cache()
     if "long_decode" in legs and args.config != 4:
-        extra.update(_extra_long_decode(stream, steps2, args.warmup))
+        extra.update(_extra_long_decode(stream, steps2, args.warmup, args.decode == "shared"))
         torch.cuda.empty_cache()
     if "mixed" in legs:
-        extra.update(_extra_mixed(stream, steps2, args.warmup))
+        extra.update(_extra_mixed(stream, steps2, args.warmup, args.decode == "shared"))
         torch.cuda.empty_cache()
     if "no_sharing" in legs and args.config == 2:
-        extra.update(_extra_no_sharing(stream, steps2, args.warmup))
+        extra.update(_extra_no_sharing(stream, steps2, args.warmup, args.decode == "shared"))
         torch.cuda.empty_cache()
         ns = extra.get("llama3_8b_decode_no_sharing", {})
         if "frac_of_hbm_peak" in ns and roof is not None:

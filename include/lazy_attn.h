@@ -407,7 +407,7 @@ LA_API la_status lazy_attn_decode_noalloc(const la_params* p, const void* q, con
  *                                   (bits 32..55), n_valid - 1 (bits 56..62)
  * It depends on the segments only (not on q_pos), so it can be reused while
  * the tables do not change.
- *   max_item_blocks  blocks per chunk (0 = 32); longer segments are cut
+ *   max_item_blocks  blocks per chunk (0 = 64); longer segments are cut
  *   info             out: the sizes below
  *   plan             host out, info->plan_bytes bytes; NULL = sizes only
  *   plan_capacity    bytes available at plan

@@ -13,17 +13,27 @@
 //     (R_m q)^T (R_{s+t} k) = (R_{m-s} q)^T (R_t k),
 // so each request's query is rotated once per item by m - s (one table row,
 // the per-document query rotation of §3.2 "Decoding", Eq. 6) and each key by
-// its in-segment index t (table rows 0 .. segment length, shared by every
-// document and hot in L2).  A document-local pool already stores R_t k: its
-// keys are used as loaded.
+// its in-segment index t = t0 + i (t0: the block's first index, i: the slot).
+// The key rotation is applied as R_{t0} R_i: a lane always holds the same slot
+// i, so its 16 pairs of row i stay in registers for the whole task, and row t0
+// is one table row per block that the 16 lanes of a k-group share (a row per
+// key would pull as many table bytes through the caches as K and V).  Rows of
+// a scaled table carry an amplitude; the slot rows are divided by it (row 0's
+// first cosine) so the key gets it once.  A document-local pool already stores
+// R_t k: its keys are used as loaded.
 //
-// Per 16-key block and wave (the waves take the chunk's blocks round-robin):
+// A wave owns one task = (item, kv head) and walks all of the item's blocks;
+// per 16-key block:
 //   S^T[16 keys x 16 cols] = K' Q^T   4 x v_mfma_f32_16x16x32_bf16 per column tile
 //   O^T[128 x 16 cols]    += V^T P^T  8 x v_mfma_f32_16x16x16_bf16 per column tile
 // with up to two column tiles of 16 (member u, head hh) columns.  The K'
-// and V^T operands are loaded and rotated once and used by every column.
-// The four waves merge through LDS and write one fp32 partial (o, m, l) per
-// (member, head); decode_shared_combine_kernel merges each request's partials.
+// and V^T operands are loaded and rotated once and used by every column.  At
+// the end the wave writes one fp32 partial (o, m, l) per (member, head)
+// straight from its registers (no LDS, no barrier);
+// decode_shared_combine_kernel merges each request's partials.  A workgroup
+// holds the tasks of four consecutive items for one kv head g, so every task
+// of head g runs on XCD g (Hkv = 8) and the member groups of one chunk, which
+// are consecutive items, share a CU and its caches.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -102,21 +112,19 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int4* __restrict__ items,
     const int4* __restrict__ members, const uint64_t* __restrict__ words,
-    const int32_t* __restrict__ q_pos, const float* __restrict__ cs, int Hkv, float qscale,
-    int interleaved, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    const int32_t* __restrict__ q_pos, const float* __restrict__ cs, int Hkv, int n_items,
+    float qscale, int interleaved, float* __restrict__ part_o, float* __restrict__ part_ml) {
   static_assert(G >= 1 && G <= 16 && NCOL % G == 0, "group size");
   constexpr bool RAW_KEYS = MODE == 1;
   const int Hq = Hkv * G;
-  const int item_idx = blockIdx.x / Hkv;  // consecutive workgroups: same item, kv heads 0..
-  const int g = blockIdx.x - item_idx * Hkv;  // (Hkv = 8: kv head g runs on XCD g)
+  const int quad = blockIdx.x / Hkv;          // items 4 quad .. 4 quad + 3
+  const int g = blockIdx.x - quad * Hkv;      // (Hkv = 8: kv head g runs on XCD g)
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;   // MFMA row (key slot) of the A operand / column of the B operand
   const int gq = lane >> 4;  // MFMA k-group
-
-  __shared__ float mo_lds[WAVES][NCOL][D];
-  __shared__ float mm_lds[WAVES][NCOL];
-  __shared__ float ml_lds[WAVES][NCOL];
+  const int item_idx = quad * WAVES + wave;
+  if (item_idx >= n_items) return;  // wave-uniform; the kernel has no barrier
 
   const int4 it = items[item_idx];  // {first word, blocks, first member, members}
   const int ncols = it.w * G;
@@ -173,6 +181,23 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
     for (int s = 0; s < 4; ++s) qbv[ct][s] = as_bf16x8(o[s]);
   }
 
+  // Slot rotation R_i of this lane's key slot i = n: pairs 32 s + 8 gq + e.
+  float cslot[2][8], sslot[2][8];
+  if (!RAW_KEYS) {
+    const float inv_amp = 1.0f / cs[0];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float* row = cs + static_cast<size_t>(n) * D + 32 * s + 8 * gq;
+      load8(row, cslot[s]);
+      load8(row + HALF, sslot[s]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        cslot[s][e] *= inv_amp;
+        sslot[s][e] *= inv_amp;
+      }
+    }
+  }
+
   float mrun[NT], lrun[NT];
   f32x4 oacc[NT][8];
 #pragma unroll
@@ -187,10 +212,10 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
   const int nblk = it.y;
   // block words one block ahead (a load at the top of the iteration would put a
   // memory round trip in front of the K/V loads)
-  uint64_t w_next = wave < nblk ? wd[wave] : 0;
-  for (int b = wave; b < nblk; b += WAVES) {
+  uint64_t w_next = wd[0];
+  for (int b = 0; b < nblk; ++b) {
     const BlockWord w = unpack_word(w_next);
-    w_next = wd[min(b + WAVES, nblk - 1)];  // past the end: a valid word, unused
+    w_next = wd[min(b + 1, nblk - 1)];  // past the end: a valid word, unused
     const size_t tile = static_cast<size_t>(w.block_id) * Hkv + g;
     const uint16_t* kb = k_pool + tile * (BS * D) + n * D;
     uint4 kr[4];
@@ -201,25 +226,29 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) vr[j] = *reinterpret_cast<const uint2*>(vb + 16 * j * BS);
 
-    // K' = R_t k with t = this lane's key index in the segment (pos0 field: the
-    // index of slot 0); unused slots read the row of the block's last key.
+    // K' = R_{t0} (R_i k): slot rotation from registers, then the block row t0
+    // (the word's pos0 field: the in-segment index of slot 0), rounded once.
     bf16x8 ka[4];
     if (RAW_KEYS) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) ka[s] = as_bf16x8(kr[s]);
     } else {
-      const int t = w.pos0 + min(n, w.n_valid - 1);
-      const float* row = cs + static_cast<size_t>(t) * D;
+      const float* row = cs + static_cast<size_t>(w.pos0) * D;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int j0 = 32 * s + 8 * gq;
-        float x1[8], x2[8], cc[8], sn[8];
+        float x1[8], x2[8], y1[8], y2[8], cc[8], sn[8];
         widen8(kr[s], x1);
         widen8(kr[s + 2], x2);
         load8(row + j0, cc);
         load8(row + HALF + j0, sn);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          y1[e] = x1[e] * cslot[s][e] - x2[e] * sslot[s][e];
+          y2[e] = x1[e] * sslot[s][e] + x2[e] * cslot[s][e];
+        }
         uint4 lo, hi;
-        rotate8(x1, x2, cc, sn, lo, hi);
+        rotate8(y1, y2, cc, sn, lo, hi);
         ka[s] = as_bf16x8(lo);
         ka[s + 2] = as_bf16x8(hi);
       }
@@ -271,43 +300,22 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
     }
   }
 
-  // Wave state -> LDS: lane (n, gq) holds O^T[16 j + 4 gq + i][column 16 ct + n].
+  // Partials straight from the registers: lane (n, gq) holds
+  // O^T[16 j + 4 gq + i][column 16 ct + n]; l is summed over the four k-groups.
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) {
+    if (ct >= nt) break;  // wave-uniform
     const float l = column_combine(lrun[ct], false);
+    const int c = 16 * ct + n;
+    if (c < ncols) {
+      const int slot = members[it.z + c / G].z;
+      const size_t ph = static_cast<size_t>(slot) * Hq + g * G + c % G;
+      float* po = part_o + ph * D + 4 * gq;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mo_lds[wave][16 * ct + n][16 * j + 4 * gq + i] = oacc[ct][j][i];
-    if (gq == 0) {
-      mm_lds[wave][16 * ct + n] = mrun[ct];
-      ml_lds[wave][16 * ct + n] = l;
-    }
-  }
-  __syncthreads();
-
-  // Merge the four waves; one fp32 partial per (member, head).
-  for (int idx = threadIdx.x; idx < ncols * D; idx += 256) {
-    const int c = idx / D;
-    const int d = idx - c * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int wv = 0; wv < WAVES; ++wv) M = fmaxf(M, mm_lds[wv][c]);
-    float O = 0.f, L = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int wv = 0; wv < WAVES; ++wv) {
-        const float f = __builtin_amdgcn_exp2f(mm_lds[wv][c] - M);
-        O += f * mo_lds[wv][c][d];
-        L += f * ml_lds[wv][c];
-      }
-    }
-    const int slot = members[it.z + c / G].z;
-    const size_t ph = static_cast<size_t>(slot) * Hq + g * G + c % G;
-    part_o[ph * D + d] = O;
-    if (d == 0) {
-      part_ml[ph * 2] = M;
-      part_ml[ph * 2 + 1] = L;
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<float4*>(po + 16 * j) =
+            float4{oacc[ct][j][0], oacc[ct][j][1], oacc[ct][j][2], oacc[ct][j][3]};
+      if (gq == 0) *reinterpret_cast<float2*>(part_ml + ph * 2) = float2{mrun[ct], l};
     }
   }
 }
@@ -347,10 +355,11 @@ template <int G, int MODE>
 hipError_t launch_g(const AttnArgs& a, const SharedPlanView& v, void* ws, hipStream_t stream) {
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o + static_cast<size_t>(v.n_partials) * a.num_q_heads * D;
-  hipLaunchKernelGGL((decode_shared_kernel<G, MODE>), dim3(v.n_items * a.num_kv_heads), dim3(256),
+  const int quads = (v.n_items + WAVES - 1) / WAVES;
+  hipLaunchKernelGGL((decode_shared_kernel<G, MODE>), dim3(quads * a.num_kv_heads), dim3(256),
                      0, stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
-                     v.items, v.members, v.words, a.q_pos, a.cos_sin, a.num_kv_heads,
+                     v.items, v.members, v.words, a.q_pos, a.cos_sin, a.num_kv_heads, v.n_items,
                      a.scale * LOG2E, a.pos_encoding == 1 ? 1 : 0, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

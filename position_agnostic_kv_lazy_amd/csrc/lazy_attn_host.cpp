@@ -218,7 +218,7 @@ struct SegKeyHash {
 };
 
 constexpr int kSharedColumns = 32;  // (member, head) columns per work item
-constexpr int kSharedDefaultChunk = 32;
+constexpr int kSharedDefaultChunk = 64;
 
 int64_t align16(int64_t x) { return (x + 15) & ~int64_t{15}; }
 

@@ -85,7 +85,7 @@ def test_plan_covers_every_key_once_config2(mib):
     assert info.members_per_item == 32 // 4
     assert np.all(items[:, 3] <= 8) and np.all(items[:, 3] >= 1)
     assert np.all(np.diff(items[:, 1]) <= 0)  # longest chunks first
-    assert info.max_item_blocks == (mib or 32) and np.all(items[:, 1] <= info.max_item_blocks)
+    assert info.max_item_blocks == (mib or 64) and np.all(items[:, 1] <= info.max_item_blocks)
     assert info.workspace_bytes == info.n_members * 32 * 130 * 4
 
 
