@@ -105,6 +105,59 @@ __device__ __forceinline__ void widen8(uint4 u, float (&x)[8]) {
   }
 }
 
+// 32-bit LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// The operands of one block from its LDS stage: four 16-byte K chunks, eight
+// 8-byte V^T pieces and (rotating pools) the 2 x 2 x 8 cos/sin values of the
+// block row this lane needs.  One asm block that waits for its own reads
+// (lgkmcnt(0)) before it ends: the compiler cannot tell which of the stage
+// loads in flight (global_load_lds) these reads depend on and would wait for
+// all of them; the caller has waited for this stage's loads (vmcnt) already.
+__device__ __forceinline__ void read_stage(uint32_t k, uint32_t v, uint32_t r, bool with_row,
+                                           uint4 (&kr)[4], uint2 (&vr)[8], uint4 (&rw)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n"
+      "ds_read_b128 %1, %12 offset:1024\n"
+      "ds_read_b128 %2, %12 offset:2048\n"
+      "ds_read_b128 %3, %12 offset:3072\n"
+      "ds_read_b64 %4, %13\n"
+      "ds_read_b64 %5, %13 offset:512\n"
+      "ds_read_b64 %6, %13 offset:1024\n"
+      "ds_read_b64 %7, %13 offset:1536\n"
+      "ds_read_b64 %8, %13 offset:2048\n"
+      "ds_read_b64 %9, %13 offset:2560\n"
+      "ds_read_b64 %10, %13 offset:3072\n"
+      "ds_read_b64 %11, %13 offset:3584\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      : "=v"(kr[0]), "=v"(kr[1]), "=v"(kr[2]), "=v"(kr[3]), "=v"(vr[0]), "=v"(vr[1]),
+        "=v"(vr[2]), "=v"(vr[3]), "=v"(vr[4]), "=v"(vr[5]), "=v"(vr[6]), "=v"(vr[7])
+      : "v"(k), "v"(v)
+      : "memory");
+  if (!with_row) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rw[i] = uint4{0u, 0u, 0u, 0u};
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %8 offset:16\n"
+        "ds_read_b128 %2, %8 offset:256\n"
+        "ds_read_b128 %3, %8 offset:272\n"
+        "ds_read_b128 %4, %8 offset:128\n"
+        "ds_read_b128 %5, %8 offset:144\n"
+        "ds_read_b128 %6, %8 offset:384\n"
+        "ds_read_b128 %7, %8 offset:400\n"
+        "s_waitcnt lgkmcnt(0)\n"
+        : "=v"(rw[0]), "=v"(rw[1]), "=v"(rw[2]), "=v"(rw[3]), "=v"(rw[4]), "=v"(rw[5]),
+          "=v"(rw[6]), "=v"(rw[7])
+        : "v"(r)
+        : "memory");
+  }
+}
+
 // MODE 0: position-free pool (keys rotated by their in-segment index);
 // MODE 1: document-local pool (keys stored as R_t k, used as loaded).
 template <int G, int MODE>
@@ -123,8 +176,11 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;   // MFMA row (key slot) of the A operand / column of the B operand
   const int gq = lane >> 4;  // MFMA k-group
-  const int item_idx = quad * WAVES + wave;
-  if (item_idx >= n_items) return;  // wave-uniform; the kernel has no barrier
+  // wave-uniform (readfirstlane tells the compiler so): the item, its block
+  // words and the rows they name are scalar loads, counted apart from the
+  // vector loads (vmcnt) that carry K and V
+  const int item_idx = __builtin_amdgcn_readfirstlane(quad * WAVES + wave);
+  if (item_idx >= n_items) return;  // the kernel has no barrier
 
   const int4 it = items[item_idx];  // {first word, blocks, first member, members}
   const int ncols = it.w * G;
@@ -208,23 +264,67 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
     for (int j = 0; j < 8; ++j) oacc[ct][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // ---- K/V (and the block's table row) go from memory straight into this
+  // wave's LDS stages (global_load_lds, no registers), one block ahead: the
+  // loads of block b + 1 are in flight while block b is computed.  The two
+  // stages are separate arrays and the loop is unrolled by two, so the
+  // compiler can tell the in-flight loads from the reads of the other stage.
+  // Per stage and wave: K tile 4 KB in MFMA A-operand order (lane l of load s
+  // holds key l & 15, dims 8 (4 s + (l >> 4)) ..), V^T tile 4 KB (lane l of load
+  // i holds dim 32 i + 16 (l >> 5) + (l & 15), keys 8 ((l >> 4) & 1) ..), and the
+  // 512-byte row t0 (written twice: lanes 32..63 repeat lanes 0..31).
+  __shared__ __attribute__((aligned(16))) uint16_t k_st0[WAVES][BS * D];
+  __shared__ __attribute__((aligned(16))) uint16_t k_st1[WAVES][BS * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_st0[WAVES][D * BS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_st1[WAVES][D * BS];
+  __shared__ __attribute__((aligned(16))) float r_st0[WAVES][2 * D];
+  __shared__ __attribute__((aligned(16))) float r_st1[WAVES][2 * D];
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t k_lane = static_cast<uint32_t>(n * D + 8 * gq);
+  const uint32_t v_lane = static_cast<uint32_t>((16 * (lane >> 5) + n) * BS + 8 * ((lane >> 4) & 1));
+  const uint32_t r_lane = static_cast<uint32_t>(4 * (lane & 31));
+  auto dma = [&](uint64_t word, uint16_t* kdst, uint16_t* vdst, float* rdst) {
+    const BlockWord w = unpack_word(word);
+    const size_t tile = static_cast<size_t>(w.block_id) * Hkv + g;
+    const uint16_t* kb = k_pool + tile * (BS * D) + k_lane;
+    const uint16_t* vb = v_pool + tile * (D * BS) + v_lane;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      __builtin_amdgcn_global_load_lds(kb + 32 * s, kdst + 512 * s, 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(vb + 512 * i, vdst + 512 * i, 16, 0, 0);
+    if (!RAW_KEYS)
+      __builtin_amdgcn_global_load_lds(cs + static_cast<size_t>(w.pos0) * D + r_lane, rdst, 16,
+                                       0, 0);
+  };
+  // offsets of this lane's operands inside a stage
+  const int k_rd = 8 * lane;  // + 512 s
+  const int v_rd = 8 * (((gq >> 1) << 4) | n) + 4 * (gq & 1);  // + 512 (j >> 1) + 256 (j & 1)
+
   const uint64_t* wd = words + it.x;
   const int nblk = it.y;
-  // block words one block ahead (a load at the top of the iteration would put a
-  // memory round trip in front of the K/V loads)
-  uint64_t w_next = wd[0];
-  for (int b = 0; b < nblk; ++b) {
-    const BlockWord w = unpack_word(w_next);
-    w_next = wd[min(b + 1, nblk - 1)];  // past the end: a valid word, unused
-    const size_t tile = static_cast<size_t>(w.block_id) * Hkv + g;
-    const uint16_t* kb = k_pool + tile * (BS * D) + n * D;
+  uint64_t w_cur = wd[0];
+  uint64_t w_nxt = wd[min(1, nblk - 1)];
+  dma(w_cur, &k_st0[wv][0], &v_st0[wv][0], &r_st0[wv][0]);
+
+  auto block = [&](int b, const uint16_t* kcur, const uint16_t* vcur, const float* rcur,
+                   uint16_t* knxt, uint16_t* vnxt, float* rnxt) {
+    const BlockWord w = unpack_word(w_cur);
+    // the word two blocks ahead (a scalar load), then the next block's loads
+    const uint64_t w_nn = wd[min(b + 2, nblk - 1)];
+    dma(w_nxt, knxt, vnxt, rnxt);  // past the end: the last block again, unused
+    // this block's stage has landed once at most the next block's DMA (8 or 9
+    // vector loads) is outstanding
+    if (RAW_KEYS)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     uint4 kr[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kr[s] = *reinterpret_cast<const uint4*>(kb + 8 * (4 * s + gq));
-    const uint16_t* vb = v_pool + tile * (D * BS) + n * BS + 4 * gq;
     uint2 vr[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) vr[j] = *reinterpret_cast<const uint2*>(vb + 16 * j * BS);
+    uint4 rw[8];  // cos then sin of pairs 8 gq .. + 7 (rw[0..3]: s = 0; rw[4..7]: s = 1)
+    read_stage(lds_addr(kcur + k_rd), lds_addr(vcur + v_rd), lds_addr(rcur + 8 * gq), !RAW_KEYS,
+               kr, vr, rw);
 
     // K' = R_{t0} (R_i k): slot rotation from registers, then the block row t0
     // (the word's pos0 field: the in-segment index of slot 0), rounded once.
@@ -233,15 +333,20 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s) ka[s] = as_bf16x8(kr[s]);
     } else {
-      const float* row = cs + static_cast<size_t>(w.pos0) * D;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int j0 = 32 * s + 8 * gq;
         float x1[8], x2[8], y1[8], y2[8], cc[8], sn[8];
         widen8(kr[s], x1);
         widen8(kr[s + 2], x2);
-        load8(row + j0, cc);
-        load8(row + HALF + j0, sn);
+        const uint4 c0 = rw[4 * s], c1 = rw[4 * s + 1], s0 = rw[4 * s + 2], s1 = rw[4 * s + 3];
+        const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          cc[e] = __uint_as_float(cw[e]);
+          sn[e] = __uint_as_float(sw[e]);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           y1[e] = x1[e] * cslot[s][e] - x2[e] * sslot[s][e];
@@ -298,6 +403,15 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
         oacc[ct][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_i16x4(vr[j]), pbv, oacc[ct][j],
                                                                  0, 0, 0);
     }
+    w_cur = w_nxt;
+    w_nxt = w_nn;
+  };
+  for (int b = 0; b < nblk; b += 2) {
+    block(b, &k_st0[wv][0], &v_st0[wv][0], &r_st0[wv][0], &k_st1[wv][0], &v_st1[wv][0],
+          &r_st1[wv][0]);
+    if (b + 1 < nblk)
+      block(b + 1, &k_st1[wv][0], &v_st1[wv][0], &r_st1[wv][0], &k_st0[wv][0], &v_st0[wv][0],
+            &r_st0[wv][0]);
   }
 
   // Partials straight from the registers: lane (n, gq) holds
