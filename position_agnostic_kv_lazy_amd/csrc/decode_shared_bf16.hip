@@ -48,6 +48,7 @@ constexpr int NT = 2;            // column tiles per item
 constexpr int NCOL = 16 * NT;    // (member, head) columns per item
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -385,15 +386,23 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
       }
       float bm = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
       bm = column_combine(bm, true);
-      const float mnew = fmaxf(mrun[ct], bm);
-      const float alpha = __builtin_amdgcn_exp2f(mrun[ct] - mnew);
+      // The column's softmax reference mrun is raised only when the block max
+      // exceeds it by more than 2^8 (or is the first finite one): then O and l
+      // are rescaled.  Any reference is exact (it cancels in O / l) and this
+      // one keeps p <= 2^8; the rescale of O, the costliest part of the online
+      // softmax, becomes rare.
+      const bool raise = bm > mrun[ct] + RESCALE_THRESHOLD;  // -inf reference: any finite bm
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float alpha = raise ? __builtin_amdgcn_exp2f(mrun[ct] - bm) : 1.0f;
+        if (raise) mrun[ct] = bm;
+        lrun[ct] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) oacc[ct][j] *= alpha;
+      }
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sacc[i] - mnew);
-      lrun[ct] = lrun[ct] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-      mrun[ct] = mnew;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) oacc[ct][j] *= alpha;
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sacc[i] - mrun[ct]);
+      lrun[ct] += (p[0] + p[1]) + (p[2] + p[3]);
       uint2 pb;
       pb.x = pack_bf16x2(p[0], p[1]);
       pb.y = pack_bf16x2(p[2], p[3]);
