@@ -187,6 +187,53 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
   const int ncols = it.w * G;
   const int nt = (ncols + 15) >> 4;  // column tiles in use (wave-uniform)
 
+  // ---- K/V (and the block's table row) go from memory straight into this
+  // wave's LDS stages (global_load_lds, no registers), one block ahead: the
+  // loads of block b + 1 are in flight while block b is computed.  The two
+  // stages are separate arrays and the loop is unrolled by two, so the
+  // compiler can tell the in-flight loads from the reads of the other stage.
+  // Per stage and wave: K tile 4 KB in MFMA A-operand order (lane l of load s
+  // holds key l & 15, dims 8 (4 s + (l >> 4)) ..), V^T tile 4 KB (lane l of load
+  // i holds dim 32 i + 16 (l >> 5) + (l & 15), keys 8 ((l >> 4) & 1) ..), and the
+  // 512-byte row t0 (written twice: lanes 32..63 repeat lanes 0..31).
+  __shared__ __attribute__((aligned(16))) uint16_t k_st0[WAVES][BS * D];
+  __shared__ __attribute__((aligned(16))) uint16_t k_st1[WAVES][BS * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_st0[WAVES][D * BS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_st1[WAVES][D * BS];
+  __shared__ __attribute__((aligned(16))) float r_st0[WAVES][2 * D];
+  __shared__ __attribute__((aligned(16))) float r_st1[WAVES][2 * D];
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t k_lane = static_cast<uint32_t>(n * D + 8 * gq);
+  const uint32_t v_lane = static_cast<uint32_t>((16 * (lane >> 5) + n) * BS + 8 * ((lane >> 4) & 1));
+  const uint32_t r_lane = static_cast<uint32_t>(4 * (lane & 31));
+  auto dma = [&](uint64_t word, uint16_t* kdst, uint16_t* vdst, float* rdst) {
+    const BlockWord w = unpack_word(word);
+    const size_t tile = static_cast<size_t>(w.block_id) * Hkv + g;
+    const uint16_t* kb = k_pool + tile * (BS * D) + k_lane;
+    const uint16_t* vb = v_pool + tile * (D * BS) + v_lane;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      __builtin_amdgcn_global_load_lds(kb + 32 * s, kdst + 512 * s, 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(vb + 512 * i, vdst + 512 * i, 16, 0, 0);
+    if (!RAW_KEYS)
+      __builtin_amdgcn_global_load_lds(cs + static_cast<size_t>(w.pos0) * D + r_lane, rdst, 16,
+                                       0, 0);
+  };
+  // offsets of this lane's operands inside a stage
+  const int k_rd = 8 * lane;  // + 512 s
+  const int v_rd = 8 * (((gq >> 1) << 4) | n) + 4 * (gq & 1);  // + 512 (j >> 1) + 256 (j & 1)
+
+  const uint64_t* wd = words + it.x;
+  const int nblk = it.y;
+  uint64_t w_cur = wd[0];
+  uint64_t w_nxt = wd[min(1, nblk - 1)];
+  // block 0's loads go out first: the query prologue below (member, q_pos,
+  // then q and its table row, three dependent round trips) overlaps them
+  dma(w_cur, &k_st0[wv][0], &v_st0[wv][0], &r_st0[wv][0]);
+
+
   // ---- queries: column c = 16 ct + n is (member c / G, head c % G), rotated
   // once by m - s and scaled by scale * log2(e), straight into the B operand.
   bf16x8 qbv[NT][4];
@@ -264,50 +311,6 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) oacc[ct][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  // ---- K/V (and the block's table row) go from memory straight into this
-  // wave's LDS stages (global_load_lds, no registers), one block ahead: the
-  // loads of block b + 1 are in flight while block b is computed.  The two
-  // stages are separate arrays and the loop is unrolled by two, so the
-  // compiler can tell the in-flight loads from the reads of the other stage.
-  // Per stage and wave: K tile 4 KB in MFMA A-operand order (lane l of load s
-  // holds key l & 15, dims 8 (4 s + (l >> 4)) ..), V^T tile 4 KB (lane l of load
-  // i holds dim 32 i + 16 (l >> 5) + (l & 15), keys 8 ((l >> 4) & 1) ..), and the
-  // 512-byte row t0 (written twice: lanes 32..63 repeat lanes 0..31).
-  __shared__ __attribute__((aligned(16))) uint16_t k_st0[WAVES][BS * D];
-  __shared__ __attribute__((aligned(16))) uint16_t k_st1[WAVES][BS * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_st0[WAVES][D * BS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_st1[WAVES][D * BS];
-  __shared__ __attribute__((aligned(16))) float r_st0[WAVES][2 * D];
-  __shared__ __attribute__((aligned(16))) float r_st1[WAVES][2 * D];
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t k_lane = static_cast<uint32_t>(n * D + 8 * gq);
-  const uint32_t v_lane = static_cast<uint32_t>((16 * (lane >> 5) + n) * BS + 8 * ((lane >> 4) & 1));
-  const uint32_t r_lane = static_cast<uint32_t>(4 * (lane & 31));
-  auto dma = [&](uint64_t word, uint16_t* kdst, uint16_t* vdst, float* rdst) {
-    const BlockWord w = unpack_word(word);
-    const size_t tile = static_cast<size_t>(w.block_id) * Hkv + g;
-    const uint16_t* kb = k_pool + tile * (BS * D) + k_lane;
-    const uint16_t* vb = v_pool + tile * (D * BS) + v_lane;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      __builtin_amdgcn_global_load_lds(kb + 32 * s, kdst + 512 * s, 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(vb + 512 * i, vdst + 512 * i, 16, 0, 0);
-    if (!RAW_KEYS)
-      __builtin_amdgcn_global_load_lds(cs + static_cast<size_t>(w.pos0) * D + r_lane, rdst, 16,
-                                       0, 0);
-  };
-  // offsets of this lane's operands inside a stage
-  const int k_rd = 8 * lane;  // + 512 s
-  const int v_rd = 8 * (((gq >> 1) << 4) | n) + 4 * (gq & 1);  // + 512 (j >> 1) + 256 (j & 1)
-
-  const uint64_t* wd = words + it.x;
-  const int nblk = it.y;
-  uint64_t w_cur = wd[0];
-  uint64_t w_nxt = wd[min(1, nblk - 1)];
-  dma(w_cur, &k_st0[wv][0], &v_st0[wv][0], &r_st0[wv][0]);
 
   auto block = [&](int b, const uint16_t* kcur, const uint16_t* vcur, const float* rcur,
                    uint16_t* knxt, uint16_t* vnxt, float* rnxt) {
