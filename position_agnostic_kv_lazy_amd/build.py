@@ -23,8 +23,12 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblazyattn.so")
 
-SOURCES = ["lazy_attn_host.cpp", "attn_f32.hip", "decode_bf16.hip", "decode_shared_bf16.hip",
-           "prefill_bf16.hip", "store_kv.hip", "cache_sim.cpp"]
+SOURCES = ["lazy_attn_host.cpp", "decode_split.cpp", "attn_f32.hip", "decode_bf16.hip",
+           "decode_shared_bf16.hip", "prefill_bf16.hip", "store_kv.hip", "cache_sim.cpp"]
+# host-only build with AddressSanitizer + UndefinedBehaviorSanitizer (no device code)
+SANITIZE_SOURCES = ["lazy_attn_host.cpp", "decode_split.cpp", "cache_sim.cpp", "host_only_stubs.cpp"]
+SANITIZE_LIB = os.path.join(BUILD, "sanitize", "liblazyattn_sanitized.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = os.environ.get("LAZYATTN_ARCH", "gfx950")
 
 
@@ -68,6 +72,34 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(verbose: bool = False) -> str:
+    """Host layer only, g++ with -fsanitize=address,undefined, for CPU tests.
+
+    Load it with the sanitizer runtime preloaded, e.g.
+        LD_PRELOAD=$(g++ -print-file-name=libasan.so) ASAN_OPTIONS=detect_leaks=0 \
+        LAZYATTN_LIB=position_agnostic_kv_lazy_amd/_build/sanitize/liblazyattn_sanitized.so \
+        python -m pytest tests/test_abi.py tests/test_cache_sim.py tests/test_shared_plan.py
+    (tests/test_sanitized_host.py runs exactly that).
+    """
+    out = os.path.dirname(SANITIZE_LIB)
+    os.makedirs(out, exist_ok=True)
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fPIC", "-shared",
+           "-fvisibility=hidden", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-I", CSRC, "-I", os.path.join(ROCM, "include")]
+    cmd += [os.path.join(CSRC, f) for f in SANITIZE_SOURCES]
+    cmd += ["-L", os.path.join(ROCM, "lib"), "-Wl,-rpath," + os.path.join(ROCM, "lib"),
+            "-lamdhip64", "-lpthread", "-o", SANITIZE_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitizer build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {SANITIZE_LIB}")
+    return SANITIZE_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -482,10 +482,12 @@ hipError_t launch_g(const AttnArgs& a, const SharedPlanView& v, void* ws, hipStr
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o + static_cast<size_t>(v.n_partials) * a.num_q_heads * D;
   const int quads = (v.n_items + WAVES - 1) / WAVES;
+  const int4* items = reinterpret_cast<const int4*>(v.items);
+  const int4* members = reinterpret_cast<const int4*>(v.members);
   hipLaunchKernelGGL((decode_shared_kernel<G, MODE>), dim3(quads * a.num_kv_heads), dim3(256),
                      0, stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
-                     v.items, v.members, v.words, a.q_pos, a.cos_sin, a.num_kv_heads, v.n_items,
+                     items, members, v.words, a.q_pos, a.cos_sin, a.num_kv_heads, v.n_items,
                      a.scale * LOG2E, a.pos_encoding == 1 ? 1 : 0, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -496,10 +498,6 @@ hipError_t launch_g(const AttnArgs& a, const SharedPlanView& v, void* ws, hipStr
 }
 
 }  // namespace
-
-size_t decode_shared_workspace_bytes(int n_partials, int num_q_heads) {
-  return static_cast<size_t>(n_partials) * num_q_heads * (D + 2) * sizeof(float);
-}
 
 hipError_t launch_decode_shared_bf16(const AttnArgs& a, const SharedPlanView& v, void* workspace,
                                      hipStream_t stream) {

@@ -2,7 +2,8 @@
 // Every launcher enqueues on `stream` and returns the hipError_t of the launch.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace lazyattn {
@@ -56,8 +57,8 @@ hipError_t decode_scratch_ptr(void** out);
 
 // Device views into a shared-segment decode plan blob (layout in lazy_attn.h).
 struct SharedPlanView {
-  const int4* items;             // {first word, blocks, first member, members}
-  const int4* members;           // {request, segment start, partial slot, 0}
+  const int32_t* items;          // int32 x 4 each: {first word, blocks, first member, members}
+  const int32_t* members;        // int32 x 4 each: {request, segment start, partial slot, 0}
   const int32_t* req_part_start; // [batch + 1]
   const uint64_t* words;         // per chunk block: id | slot-0 index << 32 | (n_valid-1) << 56
   int n_items;

@@ -820,8 +820,8 @@ LA_API la_status lazy_attn_decode_shared(const la_params* p, const la_shared_pla
                   need, workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
     const char* base = static_cast<const char*>(plan);
     lazyattn::SharedPlanView v;
-    v.items = reinterpret_cast<const int4*>(base);
-    v.members = reinterpret_cast<const int4*>(base + off.members);
+    v.items = reinterpret_cast<const int32_t*>(base);
+    v.members = reinterpret_cast<const int32_t*>(base + off.members);
     v.req_part_start = reinterpret_cast<const int32_t*>(base + off.req_part_start);
     v.words = reinterpret_cast<const uint64_t*>(base + off.words);
     v.n_items = info->n_items;

@@ -118,12 +118,19 @@ def test_config2_fp32_mode():
     _check(w, run_decode(w, requests=range(w.batch)), range(w.batch), "cfg2-f32", out, lse)
 
 
-def test_config4_sampled():
+def test_config4_every_request():
     w = config(4)
-    log("config 4 full size (64K context), sampled requests")
+    log("config 4 full size (64K context), all 16 requests")
     out, lse, _ = Device(w).run(w)
-    reqs = [0, 7, 15]
-    _check(w, run_decode(w, requests=reqs), reqs, "cfg4", out, lse)
+    _check(w, run_decode(w), range(w.batch), "cfg4", out, lse)
+
+
+def test_config2_fp32_mode_full_size():
+    """fp32 test mode at the full Llama-3-8B decode shape (64 x 5,184 keys)."""
+    w = config(2, dtype="f32")
+    log("config 2 full size, fp32 mode")
+    out, lse, _ = Device(w).run(w)
+    _check(w, run_decode(w), range(w.batch), "cfg2-f32-full", out, lse)
 
 
 def test_config5_decode_sampled():
