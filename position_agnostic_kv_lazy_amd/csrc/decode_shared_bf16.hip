@@ -446,30 +446,69 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
   }
 }
 
-// Merge each request's partials: one wave per (request, query head).
-__global__ __launch_bounds__(64) void decode_shared_combine_kernel(
+// Merge each request's partials: one wave per (request, query head), four per
+// workgroup.  Lane i takes partials i, i + 64, ... for the row statistics (one
+// load each, all in flight together, then a wave max and sum); the o rows
+// (lane l: dims 2l, 2l + 1) are then swept eight partials at a time, their
+// weights broadcast from the lane that computed them, so every load of the
+// sweep is independent of the others.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__global__ __launch_bounds__(256) void decode_shared_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ req_part_start, int Hq, uint16_t* __restrict__ out,
+    const int32_t* __restrict__ req_part_start, int Hq, int rows, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
-  const int rh = blockIdx.x;
+  const int rh = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (rh >= rows) return;  // wave-uniform; no barrier in this kernel
+  const int lane = threadIdx.x & 63;
   const int r = rh / Hq;
   const int h = rh - r * Hq;
-  const int lane = threadIdx.x;
-  const int s0 = req_part_start[r], s1 = req_part_start[r + 1];
+  const int s0 = req_part_start[r];
+  const int np = req_part_start[r + 1] - s0;
+  const float* ml = part_ml + (static_cast<size_t>(s0) * Hq + h) * 2;  // partial i: ml[2 Hq i]
+  const float* po = part_o + (static_cast<size_t>(s0) * Hq + h) * D + 2 * lane;
+  const size_t ml_step = static_cast<size_t>(Hq) * 2;
+  const size_t o_step = static_cast<size_t>(Hq) * D;
+
   float M = -INFINITY;
-  for (int s = s0; s < s1; ++s) M = fmaxf(M, part_ml[(static_cast<size_t>(s) * Hq + h) * 2]);
+  for (int i = lane; i < np; i += 64) M = fmaxf(M, ml[i * ml_step]);
+  M = wave_max(M);
   float o0 = 0.f, o1 = 0.f, L = 0.f;
   if (M != -INFINITY) {
-    for (int s = s0; s < s1; ++s) {
-      const size_t ph = static_cast<size_t>(s) * Hq + h;
-      const float ms = part_ml[ph * 2];
-      if (ms == -INFINITY) continue;
-      const float f = __builtin_amdgcn_exp2f(ms - M);
-      const float2 o = *reinterpret_cast<const float2*>(part_o + ph * D + 2 * lane);
-      o0 += f * o.x;
-      o1 += f * o.y;
-      L += f * part_ml[ph * 2 + 1];
+    for (int base = 0; base < np; base += 64) {
+      const int i = base + lane;
+      float f = 0.f;
+      if (i < np) {
+        const float2 st = *reinterpret_cast<const float2*>(ml + i * ml_step);
+        f = st.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.x - M);
+        L += f * st.y;
+      }
+      const int cnt = min(64, np - base);
+      int j = 0;
+      for (; j + 8 <= cnt; j += 8) {
+        float2 o[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          o[u] = *reinterpret_cast<const float2*>(po + (base + j + u) * o_step);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float fw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j + u));
+          o0 += fw * o[u].x;
+          o1 += fw * o[u].y;
+        }
+      }
+      for (; j < cnt; ++j) {
+        const float2 o = *reinterpret_cast<const float2*>(po + (base + j) * o_step);
+        const float fw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j));
+        o0 += fw * o.x;
+        o1 += fw * o.y;
+      }
     }
+    L = wave_sum(L);
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   *reinterpret_cast<uint32_t*>(out + static_cast<size_t>(rh) * D + 2 * lane) =
@@ -491,8 +530,9 @@ hipError_t launch_g(const AttnArgs& a, const SharedPlanView& v, void* ws, hipStr
                      a.scale * LOG2E, a.pos_encoding == 1 ? 1 : 0, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_shared_combine_kernel, dim3(a.batch * a.num_q_heads), dim3(64), 0,
-                     stream, part_o, part_ml, v.req_part_start, a.num_q_heads,
+  const int rows = a.batch * a.num_q_heads;
+  hipLaunchKernelGGL(decode_shared_combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream,
+                     part_o, part_ml, v.req_part_start, a.num_q_heads, rows,
                      static_cast<uint16_t*>(a.out), a.lse);
   return hipGetLastError();
 }
