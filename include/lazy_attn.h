@@ -407,7 +407,12 @@ LA_API la_status lazy_attn_decode_noalloc(const la_params* p, const void* q, con
  *                                   (bits 32..55), n_valid - 1 (bits 56..62)
  * It depends on the segments only (not on q_pos), so it can be reused while
  * the tables do not change.
- *   max_item_blocks  blocks per chunk (0 = 64); longer segments are cut
+ *   max_item_blocks  blocks per chunk; longer segments are cut.  0 = automatic:
+ *                    64, unless that gives fewer tasks (items x kv heads) than
+ *                    the wave slots of p->target_workgroups workgroups of four
+ *                    waves (0 = 512); then the length from {16, 24, 32, 48, 64}
+ *                    whose longest-first schedule over those slots has the
+ *                    shortest estimated makespan
  *   info             out: the sizes below
  *   plan             host out, info->plan_bytes bytes; NULL = sizes only
  *   plan_capacity    bytes available at plan

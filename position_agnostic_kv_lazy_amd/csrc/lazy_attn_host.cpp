@@ -4,6 +4,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <functional>
+#include <queue>
 #include <cstdarg>
 #include <cstdio>
 #include <climits>
@@ -219,6 +221,40 @@ struct SegKeyHash {
 
 constexpr int kSharedColumns = 32;  // (member, head) columns per work item
 constexpr int kSharedDefaultChunk = 64;
+constexpr int kSharedWavesPerWorkgroup = 4;
+
+// Estimated makespan of the shared decode's tasks (one per item and kv head)
+// when `slots` waves take them longest first: each task costs a fixed
+// prologue plus its blocks, a block with two column tiles a little more.  Used
+// only to choose the chunk length of a launch that leaves wave slots idle.
+double lpt_makespan(const std::vector<int64_t>& seg_blocks_of_group,
+                    const std::vector<int64_t>& members_of_group, int64_t chunk, int64_t C,
+                    int G, int Hkv, int64_t slots) {
+  constexpr double kPrologue = 4.0, kTwoTiles = 1.2;
+  std::vector<double> cost;
+  for (size_t g = 0; g < seg_blocks_of_group.size(); ++g) {
+    const int64_t nb = seg_blocks_of_group[g], nm = members_of_group[g];
+    for (int64_t c0 = 0; c0 < nb; c0 += chunk) {
+      const int64_t blk = std::min(chunk, nb - c0);
+      for (int64_t m0 = 0; m0 < nm; m0 += C) {
+        const int64_t cols = std::min(C, nm - m0) * G;
+        const double t = kPrologue + static_cast<double>(blk) * (cols > 16 ? kTwoTiles : 1.0);
+        for (int h = 0; h < Hkv; ++h) cost.push_back(t);
+      }
+    }
+  }
+  std::sort(cost.begin(), cost.end(), std::greater<double>());
+  std::priority_queue<double, std::vector<double>, std::greater<double>> load;
+  for (int64_t i = 0; i < slots; ++i) load.push(0.0);
+  double span = 0.0;
+  for (double t : cost) {
+    const double x = load.top() + t;
+    load.pop();
+    load.push(x);
+    span = std::max(span, x);
+  }
+  return span;
+}
 
 int64_t align16(int64_t x) { return (x + 15) & ~int64_t{15}; }
 
@@ -676,7 +712,6 @@ LA_API la_status lazy_attn_plan_shared_decode(
     const int64_t BS = p->block_size;
     const int G = p->num_q_heads / p->num_kv_heads;
     const int64_t C = kSharedColumns / G;  // members per item
-    const int64_t MIB = max_item_blocks > 0 ? max_item_blocks : kSharedDefaultChunk;
 
     // Group identical segments; every (request, segment chunk) gets one
     // partial slot, numbered request by request (the merge reads a range).
@@ -694,7 +729,6 @@ LA_API la_status lazy_attn_plan_shared_decode(
     std::vector<int32_t> req_part_start(static_cast<size_t>(batch) + 1);
     int64_t slot = 0;
     for (int r = 0; r < batch; ++r) {
-      req_part_start[r] = static_cast<int32_t>(slot);
       for (int64_t s = req_seg_start[r]; s < req_seg_start[r + 1]; ++s) {
         const int64_t nb = (seg_len[s] + BS - 1) / BS;
         const SegKey key{seg_blocks + seg_blk_start[s], nb, seg_len[s]};
@@ -707,12 +741,60 @@ LA_API la_status lazy_attn_plan_shared_decode(
         } else {
           gi = it->second;
         }
-        groups[gi].members.push_back(Member{r, seg_start[s], slot});
-        slot += (nb + MIB - 1) / MIB;
-        if (slot > INT32_MAX / 2) return fail(LA_ERR_INVALID_ARG, "too many segment chunks");
+        groups[gi].members.push_back(Member{r, seg_start[s], s});  // first_slot set below
+        slot += nb;
+        if (slot > INT32_MAX / 2) return fail(LA_ERR_INVALID_ARG, "too many segment blocks");
       }
     }
+    // Chunk length.  By default 64 blocks; when that leaves wave slots idle
+    // (one task per item and kv head, fewer than the slots of the target
+    // workgroup count), the length from {16, 24, 32, 48, 64} whose longest-
+    // first schedule has the shortest estimated makespan: a launch that fits
+    // in one round of tasks lasts as long as its longest task.
+    int64_t MIB = max_item_blocks > 0 ? max_item_blocks : kSharedDefaultChunk;
+    if (max_item_blocks == 0) {
+      std::vector<int64_t> gblk, gmem;
+      int64_t tasks64 = 0;
+      for (const Group& gr : groups) {
+        gblk.push_back((seg_len[gr.seg] + BS - 1) / BS);
+        gmem.push_back(static_cast<int64_t>(gr.members.size()));
+        tasks64 += ((gblk.back() + 63) / 64) * ((gmem.back() + C - 1) / C) * p->num_kv_heads;
+      }
+      const int64_t slots =
+          static_cast<int64_t>(p->target_workgroups > 0 ? p->target_workgroups : 512) *
+          kSharedWavesPerWorkgroup;
+      if (tasks64 < slots) {
+        double best = -1.0;
+        for (int64_t c : {64, 48, 32, 24, 16}) {  // ties keep the longer chunk
+          const double span = lpt_makespan(gblk, gmem, c, C, G, p->num_kv_heads, slots);
+          if (best < 0.0 || span < best) {
+            best = span;
+            MIB = c;
+          }
+        }
+      }
+    }
+    // partial slots, numbered request by request, one per (segment, chunk)
+    slot = 0;
+    for (int r = 0; r < batch; ++r) {
+      req_part_start[r] = static_cast<int32_t>(slot);
+      for (int64_t s = req_seg_start[r]; s < req_seg_start[r + 1]; ++s)
+        slot += ((seg_len[s] + BS - 1) / BS + MIB - 1) / MIB;
+    }
     req_part_start[batch] = static_cast<int32_t>(slot);
+    // each member's first partial slot: its segment's slots within its request
+    {
+      std::vector<int64_t> seg_slot(static_cast<size_t>(req_seg_start[batch]));
+      for (int r = 0; r < batch; ++r) {
+        int64_t k = req_part_start[r];
+        for (int64_t s = req_seg_start[r]; s < req_seg_start[r + 1]; ++s) {
+          seg_slot[s] = k;
+          k += ((seg_len[s] + BS - 1) / BS + MIB - 1) / MIB;
+        }
+      }
+      for (Group& gr : groups)
+        for (Member& mb : gr.members) mb.first_slot = seg_slot[mb.first_slot];
+    }
 
     // Items: per distinct segment, per chunk, runs of at most C members.
     struct Item {

@@ -85,8 +85,30 @@ def test_plan_covers_every_key_once_config2(mib):
     assert info.members_per_item == 32 // 4
     assert np.all(items[:, 3] <= 8) and np.all(items[:, 3] >= 1)
     assert np.all(np.diff(items[:, 1]) <= 0)  # longest chunks first
-    assert info.max_item_blocks == (mib or 64) and np.all(items[:, 1] <= info.max_item_blocks)
+    if mib:
+        assert info.max_item_blocks == mib
+    else:  # automatic: this batch leaves wave slots idle at 64, so a length is searched
+        assert info.max_item_blocks in (16, 24, 32, 48, 64)
+    assert np.all(items[:, 1] <= info.max_item_blocks)
     assert info.workspace_bytes == info.n_members * 32 * 130 * 4
+
+
+def test_automatic_chunk_length():
+    """64 blocks when the tasks fill the wave slots; a searched length otherwise."""
+    from workloads import make_no_sharing_decode
+    w = make_no_sharing_decode()  # 704 chunks x 8 kv heads > 2048 wave slots
+    p = _params(num_blocks=w.num_blocks, max_pos=w.table_rows())
+    info, _ = la.lazy_attn_plan_shared_decode(p, w.requests)
+    assert info.max_item_blocks == 64
+    w = make_config(2)  # 241 items x 8 kv heads < 2048 slots: the longest task decides
+    p = _params(num_blocks=w.num_blocks, max_pos=w.table_rows())
+    info, blob = la.lazy_attn_plan_shared_decode(p, w.requests)
+    assert info.max_item_blocks == 24
+    seen, slots, items, mem, rps = covered(info, blob)
+    assert seen == expected(_reqs(w))
+    # a larger target (more slots) does not change a launch that already fits
+    p2 = _params(num_blocks=w.num_blocks, max_pos=w.table_rows(), target_workgroups=4096)
+    assert la.lazy_attn_plan_shared_decode(p2, w.requests)[0].max_item_blocks in (16, 24, 32, 48, 64)
 
 
 def test_identical_segments_share_items():
