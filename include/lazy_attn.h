@@ -384,16 +384,21 @@ LA_API la_status lazy_attn_decode_noalloc(const la_params* p, const void* q, con
  * one physical copy of a document serve every request that lists it, at any
  * offset (§1; the same document at different offsets within one batch, §3).
  * This decode also READS each such copy once per launch for all of them: a
- * work item is a chunk of one distinct segment (a run of blocks several
- * requests list identically) together with up to 32 / G of the requests
- * holding it.  Keys are rotated by their index t within the segment, each
- * request's query once per item by m - s (score = (R_{m-s} q)^T (R_t k), the
+ * work item is a chunk of one unit -- a run of blocks, each with the index t0
+ * of its slot 0 -- together with up to 32 / G members (request r, start s)
+ * that read it; slot i of a block holds the key at logical position
+ * s + t0 + i.  A segment several requests list identically is one unit (t0
+ * counted inside the segment, s its start in each request).  In a
+ * LA_POOL_POSITION_FREE pool the segments only one request lists form that
+ * request's private run (t0 absolute, s = 0); in a LA_POOL_DOC_LOCAL pool
+ * every segment is a unit of its own.  Keys are rotated by t0 + i, each
+ * member's query once per item by m - s (score = (R_{m-s} q)^T (R_t k), the
  * per-document query rotation of §3.2 "Decoding", Eq. 6); a LA_POOL_DOC_LOCAL
- * pool already stores R_t k and is read as stored.  Every (request, chunk)
+ * pool already stores R_t k and is read as stored.  Every (member, chunk)
  * writes one fp32 partial (o, m, l) per query head; a second kernel merges
  * each request's partials.  Same results as lazy_attn_decode (the softmax
  * over exactly the listed keys) up to rounding order.
- *
+
  * lazy_attn_plan_shared_decode (host) builds the plan from the segment lists
  * lazy_attn_pack_segments takes.  Two segments are the same when they have
  * the same length and block list; their logical starts may differ.  The plan
@@ -403,16 +408,17 @@ LA_API la_status lazy_attn_decode_noalloc(const la_params* p, const void* q, con
  *     int32   req_part_start[batch + 1], padded to 16 bytes: request r owns
  *                                   partial slots req_part_start[r] ..
  *     uint64  words[n_words]        per chunk block: block id (bits 0..31),
- *                                   index of slot 0 within the segment
- *                                   (bits 32..55), n_valid - 1 (bits 56..62)
+ *                                   t0 (bits 32..55), n_valid - 1 (bits 56..62)
  * It depends on the segments only (not on q_pos), so it can be reused while
  * the tables do not change.
- *   max_item_blocks  blocks per chunk; longer segments are cut.  0 = automatic:
- *                    64, unless that gives fewer tasks (items x kv heads) than
- *                    the wave slots of p->target_workgroups workgroups of four
- *                    waves (0 = 512); then the length from {16, 24, 32, 48, 64}
- *                    whose longest-first schedule over those slots has the
- *                    shortest estimated makespan
+ *   max_item_blocks  longest chunk L, in blocks: a unit of nb blocks is cut
+ *                    into ceil(nb / L) chunks of nearly equal length.  0 =
+ *                    automatic: the L in 16, 24, .., 96 with the shortest
+ *                    launch time under a fluid model of the kernel (tasks =
+ *                    items x kv heads, started longest first on the wave slots
+ *                    of p->target_workgroups workgroups of four waves, 0 = 512;
+ *                    each block step bounded by latency or shared bandwidth;
+ *                    plus the partials' write and merge)
  *   info             out: the sizes below
  *   plan             host out, info->plan_bytes bytes; NULL = sizes only
  *   plan_capacity    bytes available at plan
@@ -425,7 +431,7 @@ typedef struct la_shared_plan_info {
   int32_t n_members;        /* (request, segment chunk) pairs = partial slots */
   int32_t n_words;          /* block words of the distinct chunks */
   int32_t members_per_item; /* at most 32 / (num_q_heads / num_kv_heads) */
-  int32_t max_item_blocks;  /* chunk length in blocks */
+  int32_t max_item_blocks;  /* longest chunk allowed, in blocks (the L used) */
   int64_t plan_bytes;       /* size of the plan blob */
   int64_t workspace_bytes;  /* device workspace lazy_attn_decode_shared needs */
 } la_shared_plan_info;

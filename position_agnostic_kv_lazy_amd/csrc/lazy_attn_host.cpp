@@ -220,40 +220,64 @@ struct SegKeyHash {
 };
 
 constexpr int kSharedColumns = 32;  // (member, head) columns per work item
-constexpr int kSharedDefaultChunk = 64;
 constexpr int kSharedWavesPerWorkgroup = 4;
+constexpr int kSharedMinChunk = 16, kSharedMaxChunk = 96;
 
-// Estimated makespan of the shared decode's tasks (one per item and kv head)
-// when `slots` waves take them longest first: each task costs a fixed
-// prologue plus its blocks, a block with two column tiles a little more.  Used
-// only to choose the chunk length of a launch that leaves wave slots idle.
-double lpt_makespan(const std::vector<int64_t>& seg_blocks_of_group,
-                    const std::vector<int64_t>& members_of_group, int64_t chunk, int64_t C,
-                    int G, int Hkv, int64_t slots) {
-  constexpr double kPrologue = 4.0, kTwoTiles = 1.2;
-  std::vector<double> cost;
-  for (size_t g = 0; g < seg_blocks_of_group.size(); ++g) {
-    const int64_t nb = seg_blocks_of_group[g], nm = members_of_group[g];
-    for (int64_t c0 = 0; c0 < nb; c0 += chunk) {
-      const int64_t blk = std::min(chunk, nb - c0);
-      for (int64_t m0 = 0; m0 < nm; m0 += C) {
-        const int64_t cols = std::min(C, nm - m0) * G;
-        const double t = kPrologue + static_cast<double>(blk) * (cols > 16 ? kTwoTiles : 1.0);
-        for (int h = 0; h < Hkv; ++h) cost.push_back(t);
-      }
+// A unit of nb blocks is cut into ceil(nb / L) chunks of nearly equal length
+// (no short tail).  Chunk k covers blocks [chunk_begin(k), chunk_begin(k + 1)).
+struct Chunking {
+  int64_t nb, n;
+  explicit Chunking(int64_t blocks, int64_t L) : nb(blocks), n((blocks + L - 1) / L) {}
+  int64_t begin(int64_t k) const { return k * nb / n; }
+};
+
+// Estimated time (us) of a shared decode launch cut at chunk length L.  A
+// fluid model of the kernel: tasks (one per item and kv head) start longest
+// first as wave slots free up; a task costs a prologue of one block step plus
+// one step per block; while n waves stream blocks together each step lasts
+// max(latency, n x block bytes / bandwidth).  The combine adds a fixed cost
+// plus writing and reading every partial once.  The constants were fitted to
+// launch times of this kernel on MI355X over four batch shapes and chunk
+// lengths 16 to 104 blocks (2.4% rms error).  The model only ranks chunk
+// lengths within that range: longer chunks leave slots idle, and with fewer
+// waves in flight the kernel streams more slowly than the model says.
+double shared_decode_time_us(const std::vector<int64_t>& unit_blocks,
+                             const std::vector<int64_t>& unit_members, int64_t L, int64_t C,
+                             int Hkv, int Hq, int64_t slots) {
+  constexpr double kStepLatencyUs = 0.8, kBytesPerUs = 5.75e6, kPrologueSteps = 1.0;
+  constexpr double kBlockBytes = 2.0 * 16 * 128 * 2;   // K and V of one block, one kv head
+  constexpr double kPartialBytes = (128 + 2) * 4 * 2;  // one partial row written and read
+  constexpr double kCombineUs = 2.0;
+  std::vector<double> work;
+  int64_t partials = 0;
+  for (size_t u = 0; u < unit_blocks.size(); ++u) {
+    const int64_t nm = unit_members[u];
+    const Chunking ch(unit_blocks[u], L);
+    partials += ch.n * nm;
+    for (int64_t k = 0; k < ch.n; ++k) {
+      const double w = kPrologueSteps + static_cast<double>(ch.begin(k + 1) - ch.begin(k));
+      for (int64_t m0 = 0; m0 < nm; m0 += C)
+        for (int h = 0; h < Hkv; ++h) work.push_back(w);
     }
   }
-  std::sort(cost.begin(), cost.end(), std::greater<double>());
-  std::priority_queue<double, std::vector<double>, std::greater<double>> load;
-  for (int64_t i = 0; i < slots; ++i) load.push(0.0);
-  double span = 0.0;
-  for (double t : cost) {
-    const double x = load.top() + t;
-    load.pop();
-    load.push(x);
-    span = std::max(span, x);
+  std::sort(work.begin(), work.end(), std::greater<double>());
+  // All running tasks advance at the same rate, so track the common progress
+  // x (steps per wave since the start) and each task's finishing x.
+  std::priority_queue<double, std::vector<double>, std::greater<double>> finish;
+  size_t next = 0;
+  double x = 0.0, t = 0.0;
+  for (; next < work.size() && static_cast<int64_t>(finish.size()) < slots; ++next)
+    finish.push(work[next]);
+  while (!finish.empty()) {
+    const double xf = finish.top();
+    const double step =
+        std::max(kStepLatencyUs, static_cast<double>(finish.size()) * kBlockBytes / kBytesPerUs);
+    t += (xf - x) * step;
+    x = xf;
+    finish.pop();
+    if (next < work.size()) finish.push(x + work[next++]);
   }
-  return span;
+  return t + kCombineUs + static_cast<double>(partials) * Hq * kPartialBytes / kBytesPerUs;
 }
 
 int64_t align16(int64_t x) { return (x + 15) & ~int64_t{15}; }
@@ -713,21 +737,19 @@ LA_API la_status lazy_attn_plan_shared_decode(
     const int G = p->num_q_heads / p->num_kv_heads;
     const int64_t C = kSharedColumns / G;  // members per item
 
-    // Group identical segments; every (request, segment chunk) gets one
-    // partial slot, numbered request by request (the merge reads a range).
-    struct Member {
+    // Group identical segments (same length and block list).
+    struct SegMember {
       int32_t r;
       int64_t start;
-      int64_t first_slot;
     };
     struct Group {
       int64_t seg;  // a representative segment: its length and blocks
-      std::vector<Member> members;
+      std::vector<SegMember> members;
     };
     std::unordered_map<SegKey, int64_t, SegKeyHash> index;
     std::vector<Group> groups;
-    std::vector<int32_t> req_part_start(static_cast<size_t>(batch) + 1);
-    int64_t slot = 0;
+    std::vector<int64_t> group_of(static_cast<size_t>(req_seg_start[batch]));
+    int64_t total_blocks = 0;
     for (int r = 0; r < batch; ++r) {
       for (int64_t s = req_seg_start[r]; s < req_seg_start[r + 1]; ++s) {
         const int64_t nb = (seg_len[s] + BS - 1) / BS;
@@ -741,89 +763,127 @@ LA_API la_status lazy_attn_plan_shared_decode(
         } else {
           gi = it->second;
         }
-        groups[gi].members.push_back(Member{r, seg_start[s], s});  // first_slot set below
-        slot += nb;
-        if (slot > INT32_MAX / 2) return fail(LA_ERR_INVALID_ARG, "too many segment blocks");
+        groups[gi].members.push_back(SegMember{r, seg_start[s]});
+        group_of[s] = gi;
+        total_blocks += nb;
+        if (total_blocks > INT32_MAX / 2)
+          return fail(LA_ERR_INVALID_ARG, "too many segment blocks");
       }
     }
-    // Chunk length.  By default 64 blocks; when that leaves wave slots idle
-    // (one task per item and kv head, fewer than the slots of the target
-    // workgroup count), the length from {16, 24, 32, 48, 64} whose longest-
-    // first schedule has the shortest estimated makespan: a launch that fits
-    // in one round of tasks lasts as long as its longest task.
-    int64_t MIB = max_item_blocks > 0 ? max_item_blocks : kSharedDefaultChunk;
-    if (max_item_blocks == 0) {
-      std::vector<int64_t> gblk, gmem;
-      int64_t tasks64 = 0;
-      for (const Group& gr : groups) {
-        gblk.push_back((seg_len[gr.seg] + BS - 1) / BS);
-        gmem.push_back(static_cast<int64_t>(gr.members.size()));
-        tasks64 += ((gblk.back() + 63) / 64) * ((gmem.back() + C - 1) / C) * p->num_kv_heads;
+
+    // Units of work: a list of blocks -- (id, index t0 of slot 0, n_valid) --
+    // read once for every member (request r, start s); slot i of a block holds
+    // the key at logical position s + t0 + i.  A segment that several requests
+    // list is one unit with t0 counted inside the segment.  In a position-free
+    // pool the segments only one request lists gain nothing from sharing: all
+    // of them form that request's private run, one unit with t0 the absolute
+    // position and s = 0 (fewer, longer items and fewer partials).  A
+    // document-local pool stores keys indexed inside their segment, so there
+    // every segment stays a unit of its own.
+    struct BlockRef {
+      int64_t id, t0;
+      int nv;
+    };
+    struct Unit {
+      std::vector<BlockRef> blocks;
+      std::vector<SegMember> members;
+    };
+    std::vector<Unit> units;
+    std::vector<std::vector<std::pair<int64_t, int64_t>>> req_units(static_cast<size_t>(batch));
+    const bool runs = p->pool_mode == LA_POOL_POSITION_FREE;
+    auto seg_blocks_of = [&](int64_t s, int64_t t_base, std::vector<BlockRef>& out) {
+      const int64_t len = seg_len[s], nb = (len + BS - 1) / BS;
+      for (int64_t k = 0; k < nb; ++k)
+        out.push_back(BlockRef{seg_blocks[seg_blk_start[s] + k], t_base + k * BS,
+                               static_cast<int>(k + 1 < nb ? BS : len - k * BS)});
+    };
+    std::vector<int64_t> unit_of_group(groups.size(), -1);
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      if (runs && groups[gi].members.size() == 1) continue;  // goes to a private run
+      unit_of_group[gi] = static_cast<int64_t>(units.size());
+      units.push_back(Unit{});
+      seg_blocks_of(groups[gi].seg, 0, units.back().blocks);
+    }
+    for (int r = 0; r < batch; ++r) {
+      int64_t run = -1;
+      for (int64_t s = req_seg_start[r]; s < req_seg_start[r + 1]; ++s) {
+        const int64_t u = unit_of_group[group_of[s]];
+        if (u >= 0) {  // a shared unit: member (r, s)
+          req_units[r].emplace_back(u, static_cast<int64_t>(units[u].members.size()));
+          units[u].members.push_back(SegMember{r, seg_start[s]});
+          continue;
+        }
+        if (run < 0) {
+          run = static_cast<int64_t>(units.size());
+          units.push_back(Unit{{}, {SegMember{r, 0}}});
+          req_units[r].emplace_back(run, 0);
+        }
+        seg_blocks_of(s, seg_start[s], units[run].blocks);
+      }
+    }
+
+    // Chunk length L.  Automatic: the L in 16, 24, .., 96 with the shortest
+    // modelled launch time on the wave slots of the target workgroup count
+    // (ties keep the longer L: fewer partials).
+    int64_t L = max_item_blocks;
+    if (L == 0) {
+      std::vector<int64_t> ublk, umem;
+      for (const Unit& u : units) {
+        ublk.push_back(static_cast<int64_t>(u.blocks.size()));
+        umem.push_back(static_cast<int64_t>(u.members.size()));
       }
       const int64_t slots =
           static_cast<int64_t>(p->target_workgroups > 0 ? p->target_workgroups : 512) *
           kSharedWavesPerWorkgroup;
-      if (tasks64 < slots) {
-        double best = -1.0;
-        for (int64_t c : {64, 48, 32, 24, 16}) {  // ties keep the longer chunk
-          const double span = lpt_makespan(gblk, gmem, c, C, G, p->num_kv_heads, slots);
-          if (best < 0.0 || span < best) {
-            best = span;
-            MIB = c;
-          }
+      double best = -1.0;
+      for (int64_t c = kSharedMaxChunk; c >= kSharedMinChunk; c -= 8) {
+        const double t =
+            shared_decode_time_us(ublk, umem, c, C, p->num_kv_heads, p->num_q_heads, slots);
+        if (best < 0.0 || t < best) {
+          best = t;
+          L = c;
         }
       }
     }
-    // partial slots, numbered request by request, one per (segment, chunk)
-    slot = 0;
+    // Partial slots, request by request (the merge reads a contiguous range):
+    // one per (unit member, chunk).
+    std::vector<std::vector<int64_t>> first_slot(units.size());
+    for (size_t u = 0; u < units.size(); ++u) first_slot[u].resize(units[u].members.size());
+    std::vector<int32_t> req_part_start(static_cast<size_t>(batch) + 1);
+    int64_t slot = 0;
     for (int r = 0; r < batch; ++r) {
       req_part_start[r] = static_cast<int32_t>(slot);
-      for (int64_t s = req_seg_start[r]; s < req_seg_start[r + 1]; ++s)
-        slot += ((seg_len[s] + BS - 1) / BS + MIB - 1) / MIB;
+      for (const auto& um : req_units[r]) {
+        first_slot[um.first][um.second] = slot;
+        slot += Chunking(static_cast<int64_t>(units[um.first].blocks.size()), L).n;
+      }
     }
     req_part_start[batch] = static_cast<int32_t>(slot);
-    // each member's first partial slot: its segment's slots within its request
-    {
-      std::vector<int64_t> seg_slot(static_cast<size_t>(req_seg_start[batch]));
-      for (int r = 0; r < batch; ++r) {
-        int64_t k = req_part_start[r];
-        for (int64_t s = req_seg_start[r]; s < req_seg_start[r + 1]; ++s) {
-          seg_slot[s] = k;
-          k += ((seg_len[s] + BS - 1) / BS + MIB - 1) / MIB;
-        }
-      }
-      for (Group& gr : groups)
-        for (Member& mb : gr.members) mb.first_slot = seg_slot[mb.first_slot];
-    }
 
-    // Items: per distinct segment, per chunk, runs of at most C members.
+    // Items: per unit, per chunk, runs of at most C members.
     struct Item {
       int32_t word0, nblk, mem0, nmem;
     };
     std::vector<Item> items;
     std::vector<int32_t> mem;  // 4 per member
     std::vector<uint64_t> words;
-    for (const Group& gr : groups) {
-      const int64_t len = seg_len[gr.seg];
-      const int64_t nb = (len + BS - 1) / BS;
-      const int64_t* blocks = seg_blocks + seg_blk_start[gr.seg];
-      for (int64_t c0 = 0, chunk = 0; c0 < nb; c0 += MIB, ++chunk) {
-        const int64_t c1 = std::min(nb, c0 + MIB);
+    for (size_t u = 0; u < units.size(); ++u) {
+      const Unit& un = units[u];
+      const Chunking ch(static_cast<int64_t>(un.blocks.size()), L);
+      for (int64_t chunk = 0; chunk < ch.n; ++chunk) {
+        const int64_t c0 = ch.begin(chunk), c1 = ch.begin(chunk + 1);
         const int64_t w0 = static_cast<int64_t>(words.size());
-        for (int64_t k = c0; k < c1; ++k) {
-          const int nv = static_cast<int>(k + 1 < nb ? BS : len - k * BS);
-          words.push_back(pack_word(blocks[k], k * BS, nv, false));
-        }
-        for (size_t m0 = 0; m0 < gr.members.size(); m0 += static_cast<size_t>(C)) {
-          const size_t m1 = std::min(gr.members.size(), m0 + static_cast<size_t>(C));
+        for (int64_t k = c0; k < c1; ++k)
+          words.push_back(pack_word(un.blocks[k].id, un.blocks[k].t0, un.blocks[k].nv, false));
+        for (size_t m0 = 0; m0 < un.members.size(); m0 += static_cast<size_t>(C)) {
+          const size_t m1 = std::min(un.members.size(), m0 + static_cast<size_t>(C));
           items.push_back(Item{static_cast<int32_t>(w0), static_cast<int32_t>(c1 - c0),
                                static_cast<int32_t>(mem.size() / 4),
                                static_cast<int32_t>(m1 - m0)});
           for (size_t m = m0; m < m1; ++m) {
-            const Member& mb = gr.members[m];
-            mem.push_back(mb.r);
-            mem.push_back(static_cast<int32_t>(mb.start));
-            mem.push_back(static_cast<int32_t>(mb.first_slot + chunk));
+            mem.push_back(un.members[m].r);
+            mem.push_back(static_cast<int32_t>(un.members[m].start));
+            mem.push_back(static_cast<int32_t>(first_slot[u][m] + chunk));
             mem.push_back(0);
           }
         }
@@ -846,7 +906,7 @@ LA_API la_status lazy_attn_plan_shared_decode(
     info->n_members = static_cast<int32_t>(n_members);
     info->n_words = static_cast<int32_t>(n_words);
     info->members_per_item = static_cast<int32_t>(C);
-    info->max_item_blocks = static_cast<int32_t>(MIB);
+    info->max_item_blocks = static_cast<int32_t>(L);
     info->plan_bytes = off.end;
     info->workspace_bytes = static_cast<int64_t>(
         lazyattn::decode_shared_workspace_bytes(static_cast<int>(n_members), p->num_q_heads));

@@ -87,28 +87,46 @@ def test_plan_covers_every_key_once_config2(mib):
     assert np.all(np.diff(items[:, 1]) <= 0)  # longest chunks first
     if mib:
         assert info.max_item_blocks == mib
-    else:  # automatic: this batch leaves wave slots idle at 64, so a length is searched
-        assert info.max_item_blocks in (16, 24, 32, 48, 64)
+    else:
+        assert 16 <= info.max_item_blocks <= 96
     assert np.all(items[:, 1] <= info.max_item_blocks)
     assert info.workspace_bytes == info.n_members * 32 * 130 * 4
 
 
 def test_automatic_chunk_length():
-    """64 blocks when the tasks fill the wave slots; a searched length otherwise."""
+    """The automatic length comes from the launch-time model over 16..96 blocks,
+    and every unit is cut into chunks of nearly equal length (no short tail)."""
     from workloads import make_no_sharing_decode
-    w = make_no_sharing_decode()  # 704 chunks x 8 kv heads > 2048 wave slots
-    p = _params(num_blocks=w.num_blocks, max_pos=w.table_rows())
-    info, _ = la.lazy_attn_plan_shared_decode(p, w.requests)
-    assert info.max_item_blocks == 64
-    w = make_config(2)  # 241 items x 8 kv heads < 2048 slots: the longest task decides
+    w = make_no_sharing_decode()  # 64 requests, each one private run of 324 blocks
     p = _params(num_blocks=w.num_blocks, max_pos=w.table_rows())
     info, blob = la.lazy_attn_plan_shared_decode(p, w.requests)
-    assert info.max_item_blocks == 24
+    assert info.max_item_blocks == 96
+    items = decode_plan(info, blob)[0]
+    # 4 chunks of 81 per request: 256 items x 8 kv heads fill the 2048 wave slots once
+    assert info.n_items == 256 and set(items[:, 1].tolist()) == {81}
+    w = make_config(2)
+    p = _params(num_blocks=w.num_blocks, max_pos=w.table_rows())
+    info, blob = la.lazy_attn_plan_shared_decode(p, w.requests)
+    assert info.max_item_blocks == 32
     seen, slots, items, mem, rps = covered(info, blob)
     assert seen == expected(_reqs(w))
-    # a larger target (more slots) does not change a launch that already fits
-    p2 = _params(num_blocks=w.num_blocks, max_pos=w.table_rows(), target_workgroups=4096)
-    assert la.lazy_attn_plan_shared_decode(p2, w.requests)[0].max_item_blocks in (16, 24, 32, 48, 64)
+    for L in (0, 24, 40):
+        info, blob = la.lazy_attn_plan_shared_decode(p, w.requests, L)
+        assert 16 <= info.max_item_blocks <= 96
+        items = decode_plan(info, blob)[0]
+        assert items[:, 1].max() <= info.max_item_blocks
+
+
+def test_chunks_of_a_unit_differ_by_at_most_one_block():
+    doc = np.arange(10)  # 10 blocks, shared by two requests
+    reqs = [[Segment(0, 160, doc, False)], [Segment(500, 160, doc, False)]]
+    p = _params(num_blocks=20, max_pos=2000)
+    for L, want in ((4, [3, 3, 4]), (3, [2, 2, 3, 3]), (10, [10]), (9, [5, 5])):
+        info, blob = la.lazy_attn_plan_shared_decode(p, reqs, L)
+        seen, _, items, _, rps = covered(info, blob)
+        assert seen == expected(reqs)
+        assert sorted(items[:, 1].tolist()) == want, L
+        assert list(np.diff(rps)) == [len(want)] * 2
 
 
 def test_identical_segments_share_items():
@@ -181,3 +199,32 @@ def test_decode_shared_checks_arguments_before_launch():
         la.lazy_attn_decode_shared(p16, info, fake, fake, fake, fake, fake, fake, 2, fake)
     with pytest.raises(la.LazyAttnError, match="aligned"):
         la.lazy_attn_decode_shared(p, info, fake + 4, fake, fake, fake, fake, fake, 2, fake)
+
+
+def test_unshared_segments_form_one_private_run():
+    """In a position-free pool a request's segments that no other request lists
+    become one unit: absolute block positions, member start 0.  A document-local
+    pool indexes keys inside their segment, so each segment stays its own unit."""
+    D = np.array([1, 2])
+    reqs = [[Segment(0, 32, D, False), Segment(32, 20, np.array([3, 4]), False),
+             Segment(52, 16, np.array([5]), False), Segment(68, 2, np.array([6]), True)],
+            [Segment(7, 32, D, False), Segment(39, 5, np.array([8]), True)]]
+    p = _params(num_blocks=20, max_pos=300)
+    info, blob = la.lazy_attn_plan_shared_decode(p, reqs)
+    seen, slots, items, mem, rps = covered(info, blob)
+    assert seen == expected(reqs)
+    # D (2 members), request 0's run (4 blocks), request 1's run (1 block)
+    assert info.n_items == 3 and info.n_words == 2 + 4 + 1
+    assert list(np.diff(rps)) == [2, 2]
+    _, _, _, words = decode_plan(info, blob)
+    runs = [it for it in items if it[3] == 1]
+    for w0, nb, m0, nm in runs:
+        assert mem[m0][1] == 0  # the member starts at 0: positions are absolute
+    t0 = ((words >> np.uint64(32)) & np.uint64(0xFFFFFF)).astype(np.int64)
+    run0 = next(it for it in runs if mem[it[2]][0] == 0)
+    assert list(t0[run0[0]:run0[0] + run0[1]]) == [32, 48, 52, 68]
+    pl = _params(num_blocks=20, max_pos=300, pool_mode="doc_local")
+    info_l, blob_l = la.lazy_attn_plan_shared_decode(pl, reqs)
+    seen_l, _, items_l, mem_l, _ = covered(info_l, blob_l)
+    assert seen_l == expected(reqs)
+    assert info_l.n_items == 1 + 3 + 1  # every segment its own unit
