@@ -65,14 +65,18 @@ def src_hash(kind):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_for(kind, workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
+def traffic_for(kind, workload, plan_sha=None):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel
+    is unchanged and, for a record taken with a shared-decode plan, the plan
+    blob is the same (the plan decides the chunks and partials)."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(f"{kind}:{workload}")
     except (OSError, ValueError):
         return None
     if not rec or rec.get("source_sha256_16") != src_hash(kind):
+        return None
+    if "plan_sha256_16" in rec and rec["plan_sha256_16"] != plan_sha:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -242,7 +246,9 @@ def run_decode_workload(w, k, v, stream, steps, warmup, split_blocks=0, cold=Tru
     }
     if shared:
         res["plan"] = {"items": db.plan_info.n_items, "partials": db.plan_info.n_members,
-                       "distinct_chunk_blocks": db.plan_info.n_words}
+                       "distinct_chunk_blocks": db.plan_info.n_words,
+                       "chunk_blocks": db.plan_info.max_item_blocks,
+                       "sha256_16": hashlib.sha256(db.host_plan.tobytes()).hexdigest()[:16]}
     if cold:
         read_sweep, write_fill = make_flushers()
         n = max(5, steps // 2)
@@ -288,7 +294,7 @@ def roofline_hbm(res, kind, workload, split):
         kern = "decode_shared_kernel + decode_shared_combine_kernel"
     else:
         kern = "decode_bf16_kernel + decode_combine_kernel" if split else "decode_bf16_kernel"
-    traffic = traffic_for(kind, workload)
+    traffic = traffic_for(kind, workload, res.get("plan", {}).get("sha256_16"))
     per_launch = {"algorithmic_bytes": res["logical_kv_bytes"],
                   "unique_bytes": res["unique_kv_bytes"],
                   "logical_gbs": round(res["logical_kv_bytes"] / (ms * 1e-3) / 1e9, 1),
@@ -474,6 +480,10 @@ def _extra_mixed(stream, steps, warmup, shared):
             "prefill_tflops": round(fl / (fm["mean"] * 1e-3) / 1e12, 1),
             "decode_logical_kv_bytes": nb, "decode_unique_kv_bytes": m5.decode.unique_kv_bytes(),
             "prefill_flops": fl, "decode_kernel": "shared" if shared else "per_request",
+            "decode_plan": None if dd.host_plan is None else {
+                "items": dd.plan_info.n_items, "partials": dd.plan_info.n_members,
+                "chunk_blocks": dd.plan_info.max_item_blocks,
+                "sha256_16": hashlib.sha256(dd.host_plan.tobytes()).hexdigest()[:16]},
             "warmup_launches": {"pair_two_streams": p2["warmup_launches"],
                                 "pair_serial": p1["warmup_launches"],
                                 "decode": dm["warmup_launches"],

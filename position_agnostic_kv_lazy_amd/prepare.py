@@ -68,6 +68,7 @@ class DeviceBatch:
     host_rbs: np.ndarray
     plan: Optional[torch.Tensor] = None       # shared-segment decode plan (device)
     plan_info: Optional[B.la_shared_plan_info] = None
+    host_plan: Optional[np.ndarray] = None    # the same plan blob on the host
 
     def run(self, stream=None):
         if self.kind == "decode" and self.plan is not None:
@@ -184,7 +185,7 @@ def prepare(w, k_dev: torch.Tensor, v_dev: torch.Tensor, device="cuda", split_bl
         cu_q = torch.from_numpy(cu).to(device)
         max_q = int(np.max(np.diff(cu)))
     ws = None
-    plan = info = None
+    plan = info = blob = None
     if w.kind == "decode" and shared:
         info, blob = B.lazy_attn_plan_shared_decode(params, w.requests, max_item_blocks)
         plan = torch.from_numpy(blob).to(device)
@@ -200,4 +201,4 @@ def prepare(w, k_dev: torch.Tensor, v_dev: torch.Tensor, device="cuda", split_bl
         cos_sin=torch.from_numpy(np.ascontiguousarray(table, np.float32)).to(device), out=out,
         lse=lse, workspace=ws,
         batch=w.batch, max_blocks=maxb, max_q=max_q, host_words=words, host_rbs=rbs,
-        plan=plan, plan_info=info)
+        plan=plan, plan_info=info, host_plan=blob)

@@ -61,6 +61,20 @@ def test_traffic_follows_the_kernel_source(bench, tmp_path, monkeypatch):
     assert bench.traffic_for("decode", "w") is None
 
 
+def test_shared_decode_traffic_follows_the_plan(bench, tmp_path, monkeypatch):
+    # a shared-decode record also names the plan blob it was taken with
+    rec = {"decode_shared:w": {"source_sha256_16": bench.src_hash("decode_shared"),
+                               "plan_sha256_16": "ab" * 8, "hbm_bytes_per_launch": 400_000_000}}
+    p = tmp_path / "traffic.json"
+    p.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
+    res = dict(_res(1_358_954_496, 0.08), decode_kernel="shared", plan={"sha256_16": "ab" * 8})
+    r = bench.roofline_hbm(res, "decode", "w", False)
+    assert r["traffic"] == 400_000_000 and r["kernel"].startswith("decode_shared_kernel")
+    res["plan"] = {"sha256_16": "cd" * 8}  # another chunking: the counters no longer apply
+    assert bench.roofline_hbm(res, "decode", "w", False)["traffic"] is None
+
+
 def test_parity_summary(bench):
     import numpy as np
     ref = [np.ones((4, 8)), np.full((4, 8), 2.0)]
