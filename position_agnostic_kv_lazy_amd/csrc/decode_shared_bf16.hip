@@ -4,16 +4,19 @@
 // serves every request that lists the document, at whatever offset s the
 // request places it ("LazyAttention" §1 and §3.1 "Deferred encoding").  This
 // kernel also reads that copy once per launch for all of those requests: a
-// work item is a chunk of one distinct segment plus up to 32 / G requests
-// holding it, and one workgroup per (item, kv head) streams the chunk's K/V
-// blocks once and scores them against all of those requests' queries.
+// work item is a chunk of one unit -- a run of blocks, each with the index t0
+// of its slot 0 -- plus up to 32 / G members (request, start s) that read it,
+// and one workgroup per (item, kv head) streams the chunk's K/V blocks once
+// and scores them against all of those members' queries.  A segment several
+// requests list is one unit (t0 counted inside the segment); the segments
+// only one request lists form its private run (t0 absolute, s = 0).
 //
-// Rotation (Fact 3.2, §3.2): for a request with query position m and the
-// segment at start s, the key at in-segment index t sits at s + t and
+// Rotation (Fact 3.2, §3.2): for a member with query position m and start s,
+// the key at index t = t0 + i of the unit sits at s + t and
 //     (R_m q)^T (R_{s+t} k) = (R_{m-s} q)^T (R_t k),
-// so each request's query is rotated once per item by m - s (one table row,
+// so each member's query is rotated once per item by m - s (one table row,
 // the per-document query rotation of §3.2 "Decoding", Eq. 6) and each key by
-// its in-segment index t = t0 + i (t0: the block's first index, i: the slot).
+// t (i: the slot).
 // The key rotation is applied as R_{t0} R_i: a lane always holds the same slot
 // i, so its 16 pairs of row i stay in registers for the whole task, and row t0
 // is one table row per block that the 16 lanes of a k-group share (a row per
@@ -159,7 +162,7 @@ __device__ __forceinline__ void read_stage(uint32_t k, uint32_t v, uint32_t r, b
   }
 }
 
-// MODE 0: position-free pool (keys rotated by their in-segment index);
+// MODE 0: position-free pool (keys rotated by their index t in the unit);
 // MODE 1: document-local pool (keys stored as R_t k, used as loaded).
 template <int G, int MODE>
 __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
                kr, vr, rw);
 
     // K' = R_{t0} (R_i k): slot rotation from registers, then the block row t0
-    // (the word's pos0 field: the in-segment index of slot 0), rounded once.
+    // (the word's pos0 field: t0, the unit index of slot 0), rounded once.
     bf16x8 ka[4];
     if (RAW_KEYS) {
 #pragma unroll
