@@ -22,8 +22,8 @@
  *    as void*, NULL = default stream) and return without synchronising.
  *    Scalar arguments are checked before anything is enqueued; the contents of
  *    device arrays are NOT checked on the device (use the host-side
- *    lazy_attn_pack_segments / lazy_attn_validate_table for that).  Malformed
- *    device tables give undefined results.
+ *    lazy_attn_pack_segments / lazy_attn_validate_table for that, or set
+ *    la_params.check_tables).  Malformed device tables give undefined results.
  *  - Calls are thread-safe; concurrent calls on one stream serialise in order.
  *
  * RoPE convention (readings of the paper, stated once here)
@@ -171,8 +171,25 @@ typedef struct la_params {
   int32_t target_workgroups; /* decode split heuristic, 0 = 512 (256 CUs x 2) */
   int32_t pool_mode;     /* la_pool_mode of k_pool (above) */
   int32_t pos_encoding;  /* la_pos_encoding (above) */
-  int32_t reserved[3];   /* must be zero */
+  int32_t check_tables;  /* nonzero: GPU entry points check their tables first (below) */
+  int32_t reserved[2];   /* must be zero */
 } la_params;
+
+/*
+ * check_tables (debugging).  When nonzero, every GPU entry point -- decode,
+ * decode_noalloc, decode_shared, prefill, store_kv -- first waits for its
+ * stream (hipStreamSynchronize), copies the tables it would read to the host
+ * and checks them: the block words, req_blk_start, q_pos and cu_q with the
+ * checks of lazy_attn_validate_table (with the call's max_blocks_per_req /
+ * max_q_per_req); a shared-decode plan against the batch (item, member and
+ * word ranges, every partial slot written exactly once and inside its
+ * request's range, block ids inside the pool, every table row the kernel
+ * reads -- |m - s|, t0 and the keys' positions -- inside max_pos); the cache
+ * write's slots (inside the pool, distinct) and rotation positions.  A table
+ * that fails returns LA_ERR_INVALID_ARG and nothing is enqueued.  Each call
+ * then costs a device synchronisation and a copy of its tables; with 0 (the
+ * default) the contents of device arrays are not checked at all.
+ */
 
 /* Human-readable name of a status code (static string). */
 LA_API const char* lazy_attn_status_string(la_status s);

@@ -72,7 +72,8 @@ class la_params(ctypes.Structure):
         ("target_workgroups", ctypes.c_int32),
         ("pool_mode", ctypes.c_int32),
         ("pos_encoding", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 3),
+        ("check_tables", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -188,7 +189,7 @@ def _check(status: int, func: str):
 
 def make_params(*, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, scale,
                 max_pos, split_blocks=0, target_workgroups=0, pool_mode=0,
-                pos_encoding=0) -> la_params:
+                pos_encoding=0, check_tables=False) -> la_params:
     p = la_params()
     p.num_q_heads = num_q_heads
     p.num_kv_heads = num_kv_heads
@@ -204,6 +205,7 @@ def make_params(*, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, 
                    "doc_local": LA_POOL_DOC_LOCAL}.get(pool_mode, pool_mode)
     p.pos_encoding = {"rope_half": LA_ROPE_HALF, "rope_interleaved": LA_ROPE_INTERLEAVED,
                       "alibi": LA_ALIBI}.get(pos_encoding, pos_encoding)
+    p.check_tables = 1 if check_tables else 0
     return p
 
 

@@ -76,7 +76,7 @@ la_status check_params(const la_params* p) {
   if (!std::isfinite(p->scale)) return fail(LA_ERR_INVALID_ARG, "scale is not finite");
   if (p->split_blocks < 0 || p->target_workgroups < 0)
     return fail(LA_ERR_INVALID_ARG, "split_blocks / target_workgroups must be >= 0");
-  for (int i = 0; i < 3; ++i)
+  for (int i = 0; i < 2; ++i)
     if (p->reserved[i] != 0) return fail(LA_ERR_INVALID_ARG, "reserved fields must be zero");
   if (p->pool_mode != LA_POOL_POSITION_FREE && p->pool_mode != LA_POOL_DOC_LOCAL)
     return fail(LA_ERR_INVALID_ARG, "unknown pool_mode %d", p->pool_mode);
@@ -293,6 +293,118 @@ PlanOffsets plan_offsets(int64_t n_items, int64_t n_members, int64_t batch, int6
   o.words = o.req_part_start + align16(4 * (batch + 1));
   o.end = o.words + 8 * n_words;
   return o;
+}
+
+// ---- la_params.check_tables: host-side checks of a call's device tables.
+
+// Waits for the stream, so the check reads what earlier work on it wrote.
+// Without a device (tables in host memory, as the CPU tests pass them) there
+// is nothing to wait for.
+la_status sync_for_check(void* stream) {
+  const hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) return LA_OK;
+  (void)hipGetLastError();
+  if (e == hipErrorNoDevice || e == hipErrorInvalidDevice) return LA_OK;
+  return hip_fail(e, "hipStreamSynchronize (check_tables)");
+}
+
+// A shared-decode plan against the batch it is launched on: every range the
+// kernels index, every partial slot written exactly once inside its request's
+// range, and every table row the kernel reads (|m - s|, t0, the keys'
+// positions) inside [0, max_pos).
+la_status check_shared_plan(const la_params* p, const la_shared_plan_info* info,
+                            const void* plan, const int32_t* q_pos, int32_t batch) {
+  std::vector<uint8_t> blob;
+  la_status st = fetch(static_cast<const uint8_t*>(plan), static_cast<size_t>(info->plan_bytes), blob);
+  if (st != LA_OK) return st;
+  std::vector<int32_t> qp;
+  if ((st = fetch(q_pos, static_cast<size_t>(batch), qp)) != LA_OK) return st;
+  const int64_t n_items = info->n_items, n_mem = info->n_members, n_words = info->n_words;
+  const PlanOffsets o = plan_offsets(n_items, n_mem, batch, n_words);
+  const int32_t* items = reinterpret_cast<const int32_t*>(blob.data());
+  const int32_t* mem = reinterpret_cast<const int32_t*>(blob.data() + o.members);
+  const int32_t* rps = reinterpret_cast<const int32_t*>(blob.data() + o.req_part_start);
+  const uint64_t* words = reinterpret_cast<const uint64_t*>(blob.data() + o.words);
+  if (rps[0] != 0 || rps[batch] != n_mem)
+    return fail(LA_ERR_INVALID_ARG, "plan: partial slots run [%d, %d), expected [0, %lld)",
+                rps[0], rps[batch], (long long)n_mem);
+  for (int r = 0; r < batch; ++r)
+    if (rps[r + 1] <= rps[r])
+      return fail(LA_ERR_INVALID_ARG, "plan: request %d has no partial slot", r);
+  const bool doc = p->pool_mode == LA_POOL_DOC_LOCAL;
+  std::vector<uint8_t> written(static_cast<size_t>(n_mem), 0);
+  for (int64_t i = 0; i < n_items; ++i) {
+    const int32_t w0 = items[4 * i], nb = items[4 * i + 1], m0 = items[4 * i + 2],
+                  nm = items[4 * i + 3];
+    if (w0 < 0 || nb < 1 || static_cast<int64_t>(w0) + nb > n_words)
+      return fail(LA_ERR_INVALID_ARG, "plan: item %lld words [%d, +%d) outside [0, %lld)",
+                  (long long)i, w0, nb, (long long)n_words);
+    if (m0 < 0 || nm < 1 || nm > info->members_per_item || static_cast<int64_t>(m0) + nm > n_mem)
+      return fail(LA_ERR_INVALID_ARG, "plan: item %lld members [%d, +%d) invalid", (long long)i,
+                  m0, nm);
+    for (int32_t k = w0; k < w0 + nb; ++k) {
+      const int64_t id = static_cast<int64_t>(words[k] & 0xFFFFFFFFull);
+      const int64_t t0 = static_cast<int64_t>((words[k] >> 32) & 0xFFFFFFull);
+      const int nv = static_cast<int>((words[k] >> 56) & 0x7Full) + 1;
+      if (id >= p->num_blocks)
+        return fail(LA_ERR_INVALID_ARG, "plan: word %d block id %lld >= num_blocks", k, (long long)id);
+      if (nv > p->block_size || (words[k] >> 63) != 0)
+        return fail(LA_ERR_INVALID_ARG, "plan: word %d is malformed", k);
+      if (!doc && t0 >= p->max_pos)
+        return fail(LA_ERR_INVALID_ARG, "plan: word %d table row %lld >= max_pos", k, (long long)t0);
+    }
+    for (int32_t m = m0; m < m0 + nm; ++m) {
+      const int32_t r = mem[4 * m], sst = mem[4 * m + 1], slot = mem[4 * m + 2];
+      if (r < 0 || r >= batch || mem[4 * m + 3] != 0 || sst < 0)
+        return fail(LA_ERR_INVALID_ARG, "plan: member %d is malformed", m);
+      if (slot < rps[r] || slot >= rps[r + 1])
+        return fail(LA_ERR_INVALID_ARG, "plan: member %d writes slot %d outside request %d's "
+                    "range [%d, %d)", m, slot, r, rps[r], rps[r + 1]);
+      if (written[slot]++ != 0)
+        return fail(LA_ERR_INVALID_ARG, "plan: partial slot %d is written twice", slot);
+      const int64_t off = static_cast<int64_t>(qp[r]) - sst;
+      if (qp[r] < 0 || (off < 0 ? -off : off) >= p->max_pos)
+        return fail(LA_ERR_INVALID_ARG, "plan: member %d query rotation row |%d - %d| >= max_pos",
+                    m, qp[r], sst);
+      for (int32_t k = w0; k < w0 + nb; ++k) {
+        const int64_t t0 = static_cast<int64_t>((words[k] >> 32) & 0xFFFFFFull);
+        const int nv = static_cast<int>((words[k] >> 56) & 0x7Full) + 1;
+        if (sst + t0 + nv - 1 >= p->max_pos)
+          return fail(LA_ERR_INVALID_ARG, "plan: member %d reads position %lld >= max_pos", m,
+                      (long long)(sst + t0 + nv - 1));
+      }
+    }
+  }
+  for (int64_t j = 0; j < n_mem; ++j)
+    if (written[j] != 1) return fail(LA_ERR_INVALID_ARG, "plan: partial slot %lld is never written", (long long)j);
+  return LA_OK;
+}
+
+// The cache write's slots (inside the pool, distinct: two writers of one slot
+// race) and rotation positions.
+la_status check_store_tables(const la_params* p, int64_t n_tokens, const int64_t* slots,
+                             const int32_t* rope_pos) {
+  std::vector<int64_t> sl;
+  la_status st = fetch(slots, static_cast<size_t>(n_tokens), sl);
+  if (st != LA_OK) return st;
+  const int64_t n_slots = p->num_blocks * p->block_size;
+  for (int64_t i = 0; i < n_tokens; ++i)
+    if (sl[i] < 0 || sl[i] >= n_slots)
+      return fail(LA_ERR_INVALID_ARG, "store_kv: token %lld slot %lld outside the pool",
+                  (long long)i, (long long)sl[i]);
+  std::sort(sl.begin(), sl.end());
+  for (int64_t i = 1; i < n_tokens; ++i)
+    if (sl[i] == sl[i - 1])
+      return fail(LA_ERR_INVALID_ARG, "store_kv: slot %lld is written twice", (long long)sl[i]);
+  if (rope_pos) {
+    std::vector<int32_t> rp;
+    if ((st = fetch(rope_pos, static_cast<size_t>(n_tokens), rp)) != LA_OK) return st;
+    for (int64_t i = 0; i < n_tokens; ++i)
+      if (rp[i] < 0 || rp[i] >= p->max_pos)
+        return fail(LA_ERR_INVALID_ARG, "store_kv: token %lld rotation position %d outside "
+                    "[0, max_pos)", (long long)i, rp[i]);
+  }
+  return LA_OK;
 }
 
 }  // namespace
@@ -616,6 +728,10 @@ LA_API la_status lazy_attn_store_kv(const la_params* p, const void* k, const voi
       return fail(LA_ERR_INVALID_ARG, "NULL device pointer passed to lazy_attn_store_kv");
     if (rope_pos && !cos_sin)
       return fail(LA_ERR_INVALID_ARG, "rope_pos given without cos_sin");
+    if (p->check_tables) {
+      if ((st = sync_for_check(stream)) != LA_OK) return st;
+      if ((st = check_store_tables(p, n_tokens, slots, rope_pos)) != LA_OK) return st;
+    }
     for (const void* ptr : {k, v, static_cast<const void*>(k_pool), static_cast<const void*>(v_pool)})
       if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
         return fail(LA_ERR_INVALID_ARG, "k, v, k_pool and v_pool must be 16-byte aligned");
@@ -644,6 +760,12 @@ LA_API la_status lazy_attn_decode(const la_params* p, const void* q, const void*
       return fail(LA_ERR_INVALID_ARG, "NULL device pointer passed to lazy_attn_decode");
     if (batch < 1 || max_blocks_per_req < 1)
       return fail(LA_ERR_INVALID_ARG, "batch and max_blocks_per_req must be >= 1");
+    if (p->check_tables) {
+      if ((st = sync_for_check(stream)) != LA_OK) return st;
+      if ((st = lazy_attn_validate_table(p, batch, blk_words, req_blk_start, q_pos, nullptr,
+                                         max_blocks_per_req, 0)) != LA_OK)
+        return st;
+    }
     const lazyattn::AttnArgs a = make_args(p, q, k_pool, v_pool, blk_words, req_blk_start, nullptr,
                                            q_pos, cos_sin, batch, 1, max_blocks_per_req, out, lse);
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -680,6 +802,12 @@ LA_API la_status lazy_attn_decode_noalloc(const la_params* p, const void* q, con
       return fail(LA_ERR_INVALID_ARG, "NULL device pointer passed to lazy_attn_decode_noalloc");
     if (batch < 1 || max_blocks_per_req < 1)
       return fail(LA_ERR_INVALID_ARG, "batch and max_blocks_per_req must be >= 1");
+    if (p->check_tables) {
+      if ((st = sync_for_check(stream)) != LA_OK) return st;
+      if ((st = lazy_attn_validate_table(p, batch, blk_words, req_blk_start, q_pos, nullptr,
+                                         max_blocks_per_req, 0)) != LA_OK)
+        return st;
+    }
     const lazyattn::AttnArgs a = make_args(p, q, k_pool, v_pool, blk_words, req_blk_start, nullptr,
                                            q_pos, cos_sin, batch, 1, max_blocks_per_req, out, lse);
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -960,6 +1088,10 @@ LA_API la_status lazy_attn_decode_shared(const la_params* p, const la_shared_pla
     if (workspace == nullptr || workspace_bytes < need)
       return fail(LA_ERR_WORKSPACE_TOO_SMALL, "shared decode needs %zu workspace bytes, got %zu",
                   need, workspace == nullptr ? static_cast<size_t>(0) : workspace_bytes);
+    if (p->check_tables) {
+      if ((st = sync_for_check(stream)) != LA_OK) return st;
+      if ((st = check_shared_plan(p, info, plan, q_pos, batch)) != LA_OK) return st;
+    }
     const char* base = static_cast<const char*>(plan);
     lazyattn::SharedPlanView v;
     v.items = reinterpret_cast<const int32_t*>(base);
@@ -995,6 +1127,12 @@ LA_API la_status lazy_attn_prefill(const la_params* p, const void* q, const void
       return fail(LA_ERR_INVALID_ARG, "batch and max_q_per_req must be >= 1");
     if (max_q_per_req > 65535 && p->dtype == LA_FP32)
       return fail(LA_ERR_UNSUPPORTED, "fp32 prefill supports at most 65535 rows per request");
+    if (p->check_tables) {
+      if ((st = sync_for_check(stream)) != LA_OK) return st;
+      if ((st = lazy_attn_validate_table(p, batch, blk_words, req_blk_start, q_pos0, cu_q, 0,
+                                         max_q_per_req)) != LA_OK)
+        return st;
+    }
     const lazyattn::AttnArgs a = make_args(p, q, k_pool, v_pool, blk_words, req_blk_start, cu_q,
                                            q_pos0, cos_sin, batch, max_q_per_req, 0, out, lse);
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -94,14 +94,14 @@ class DeviceBatch:
 
 def params_for(w, num_blocks: int, max_pos: Optional[int] = None, split_blocks: int = 0,
                target_workgroups: int = 0, pool_mode="position_free",
-               pos_encoding="rope_half") -> B.la_params:
+               pos_encoding="rope_half", check_tables: bool = False) -> B.la_params:
     """la_params describing batch w over a pool of num_blocks blocks."""
     rows = int(max_pos) if max_pos is not None else int(w.table_rows())
     return B.make_params(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                          head_dim=w.head_dim, block_size=w.block_size, num_blocks=int(num_blocks),
                          dtype=w.dtype, scale=w.scale, max_pos=rows, split_blocks=split_blocks,
                          target_workgroups=target_workgroups, pool_mode=pool_mode,
-                         pos_encoding=pos_encoding)
+                         pos_encoding=pos_encoding, check_tables=check_tables)
 
 
 def store_pool(w, k_tok: np.ndarray, v_tok: np.ndarray, slots: np.ndarray,
@@ -158,18 +158,19 @@ def prepare(w, k_dev: torch.Tensor, v_dev: torch.Tensor, device="cuda", split_bl
             target_workgroups: int = 0, max_pos: Optional[int] = None,
             pool_mode="position_free", pos_encoding="rope_half",
             table: Optional[np.ndarray] = None, shared: bool = False,
-            max_item_blocks: int = 0) -> DeviceBatch:
+            max_item_blocks: int = 0, check_tables: bool = False) -> DeviceBatch:
     """Pack and upload everything lazy_attn_decode/prefill need for batch w.
 
     table overrides the position table handed to the kernels: by default the
     RoPE cos/sin rows (lazy_attn_rope_table) or, for ALiBi, the standard
     slopes (lazy_attn_alibi_slopes).  shared=True (decode) builds a
     shared-segment plan (lazy_attn_plan_shared_decode) and runs
-    lazy_attn_decode_shared instead of lazy_attn_decode.
+    lazy_attn_decode_shared instead of lazy_attn_decode.  check_tables sets
+    la_params.check_tables (every launch checks its tables first).
     """
     rows = int(max_pos) if max_pos is not None else int(w.table_rows())
     params = params_for(w, int(k_dev.shape[0]), rows, split_blocks, target_workgroups, pool_mode,
-                        pos_encoding)
+                        pos_encoding, check_tables)
     words, rbs, maxb = B.lazy_attn_pack_segments(params, w.requests)
     if table is None:
         table = (B.lazy_attn_alibi_slopes(w.num_q_heads) if pos_encoding == "alibi"

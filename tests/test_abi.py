@@ -137,11 +137,15 @@ def test_param_validation(kw, status, msg):
         la.lazy_attn_decode_workspace_size(p, 4, 10)
 
 
-def test_reserved_fields_must_be_zero():
+@pytest.mark.parametrize("i", [0, 1])
+def test_reserved_fields_must_be_zero(i):
     p = _params()
-    p.reserved[2] = 1
+    p.reserved[i] = 1
     with pytest.raises(la.LazyAttnError, match="reserved"):
         la.lazy_attn_decode_workspace_size(p, 4, 10)
+    p = _params()
+    p.check_tables = 1  # the debugging switch is a field of its own
+    assert la.lazy_attn_decode_workspace_size(p, 4, 10) >= 0
 
 
 def test_fp32_mode_allows_head_dim_64():

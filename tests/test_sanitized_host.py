@@ -1,6 +1,6 @@
 """The C ABI's host layer under AddressSanitizer and UndefinedBehaviorSanitizer.
 
-build.py --sanitize compiles the host code (argument checks, table packer and
+build.py --sanitize compiles the host code (argument and table checks, packer and
 validator, shared-decode planner, cos/sin tables, cache simulator) with
 g++ -fsanitize=address,undefined and no device code; the CPU tests of that
 layer then run against it in a child process with the sanitizer runtime
@@ -28,7 +28,8 @@ def test_host_layer_is_clean_under_asan_and_ubsan():
     env = dict(os.environ, LD_PRELOAD=asan, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1", LAZYATTN_LIB=lib)
     t = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
-                        "tests/test_abi.py", "tests/test_cache_sim.py", "tests/test_shared_plan.py"],
+                        "tests/test_abi.py", "tests/test_cache_sim.py", "tests/test_shared_plan.py",
+                        "tests/test_check_tables.py"],
                        capture_output=True, text=True, cwd=ROOT, env=env, timeout=900)
     out = t.stdout + t.stderr
     assert t.returncode == 0, out[-4000:]
