@@ -415,13 +415,13 @@ LA_API la_status lazy_attn_decode_noalloc(const la_params* p, const void* q, con
  * writes one fp32 partial (o, m, l) per query head; a second kernel merges
  * each request's partials.  Same results as lazy_attn_decode (the softmax
  * over exactly the listed keys) up to rounding order.
-
+ *
  * lazy_attn_plan_shared_decode (host) builds the plan from the segment lists
  * lazy_attn_pack_segments takes.  Two segments are the same when they have
  * the same length and block list; their logical starts may differ.  The plan
  * is a flat blob the caller copies to device memory as is:
  *     int32x4 items[n_items]        {first word, blocks, first member, members}
- *     int32x4 members[n_members]    {request, segment start s, partial slot, 0}
+ *     int32x4 members[n_members]    {request, start s, partial slot, 0}
  *     int32   req_part_start[batch + 1], padded to 16 bytes: request r owns
  *                                   partial slots req_part_start[r] ..
  *     uint64  words[n_words]        per chunk block: block id (bits 0..31),
@@ -445,7 +445,7 @@ LA_API la_status lazy_attn_decode_noalloc(const la_params* p, const void* q, con
 typedef struct la_shared_plan_info {
   int32_t batch;            /* requests the plan covers */
   int32_t n_items;          /* work items; the launch runs n_items x num_kv_heads workgroups */
-  int32_t n_members;        /* (request, segment chunk) pairs = partial slots */
+  int32_t n_members;        /* (member, chunk) pairs = partial slots */
   int32_t n_words;          /* block words of the distinct chunks */
   int32_t members_per_item; /* at most 32 / (num_q_heads / num_kv_heads) */
   int32_t max_item_blocks;  /* longest chunk allowed, in blocks (the L used) */
@@ -466,7 +466,8 @@ LA_API la_status lazy_attn_plan_shared_decode(
  *   q, k_pool, v_pool, q_pos, cos_sin, out, lse: as for lazy_attn_decode
  *   workspace  device, >= info->workspace_bytes (the partials); clobbered
  * Requires 0 <= s + t < max_pos for every key, m < max_pos, and a plan built
- * for the same params and batch (not checked on the device).
+ * for the same params and batch (not checked on the device; check_tables in
+ * la_params checks it on the host).
  */
 LA_API la_status lazy_attn_decode_shared(const la_params* p, const la_shared_plan_info* info,
                                          const void* plan, const void* q, const void* k_pool,
