@@ -321,10 +321,14 @@ la_status check_shared_plan(const la_params* p, const la_shared_plan_info* info,
   if ((st = fetch(q_pos, static_cast<size_t>(batch), qp)) != LA_OK) return st;
   const int64_t n_items = info->n_items, n_mem = info->n_members, n_words = info->n_words;
   const PlanOffsets o = plan_offsets(n_items, n_mem, batch, n_words);
-  const int32_t* items = reinterpret_cast<const int32_t*>(blob.data());
-  const int32_t* mem = reinterpret_cast<const int32_t*>(blob.data() + o.members);
-  const int32_t* rps = reinterpret_cast<const int32_t*>(blob.data() + o.req_part_start);
-  const uint64_t* words = reinterpret_cast<const uint64_t*>(blob.data() + o.words);
+  // typed copies of the sections (the caller checked plan_bytes == o.end)
+  std::vector<int32_t> items(static_cast<size_t>(4 * n_items)), mem(static_cast<size_t>(4 * n_mem)),
+      rps(static_cast<size_t>(batch) + 1);
+  std::vector<uint64_t> words(static_cast<size_t>(n_words));
+  std::memcpy(items.data(), blob.data(), items.size() * sizeof(int32_t));
+  std::memcpy(mem.data(), blob.data() + o.members, mem.size() * sizeof(int32_t));
+  std::memcpy(rps.data(), blob.data() + o.req_part_start, rps.size() * sizeof(int32_t));
+  std::memcpy(words.data(), blob.data() + o.words, words.size() * sizeof(uint64_t));
   if (rps[0] != 0 || rps[batch] != n_mem)
     return fail(LA_ERR_INVALID_ARG, "plan: partial slots run [%d, %d), expected [0, %lld)",
                 rps[0], rps[batch], (long long)n_mem);
