@@ -436,7 +436,10 @@ LA_API la_status lazy_attn_decode_noalloc(const la_params* p, const void* q, con
  *                    of p->target_workgroups workgroups of four waves, 0 = 512;
  *                    each block step bounded by latency or shared bandwidth;
  *                    plus the partials' write and merge)
- *   info             out: the sizes below
+ *   info             out: the sizes below, and the L used (passing it back
+ *                    as max_item_blocks gives the same plan without the
+ *                    search: a caller sizing the blob first, or reusing L
+ *                    across steps, pays for the search once)
  *   plan             host out, info->plan_bytes bytes; NULL = sizes only
  *   plan_capacity    bytes available at plan
  * bf16 only (LA_ERR_UNSUPPORTED for LA_FP32 and LA_ALIBI); the same checks

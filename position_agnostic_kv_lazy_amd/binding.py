@@ -286,16 +286,21 @@ def _segment_arrays(requests):
 
 def lazy_attn_plan_shared_decode(params: la_params, requests: Sequence[Sequence],
                                  max_item_blocks: int = 0):
-    """Shared-segment decode plan: (la_shared_plan_info, plan blob as uint8 numpy)."""
+    """Shared-segment decode plan: (la_shared_plan_info, plan blob as uint8 numpy).
+
+    The first call returns the sizes and the chunk length it chose; the
+    second passes that length back, which gives the same plan without
+    searching again."""
     a_req, a_st, a_len, a_new, a_bs, a_bl = _segment_arrays(requests)
     info = la_shared_plan_info()
     args = (ctypes.byref(params), len(requests), a_req.ctypes.data_as(_i64p),
             a_st.ctypes.data_as(_i64p), a_len.ctypes.data_as(_i64p), a_new.ctypes.data_as(_u8p),
-            a_bs.ctypes.data_as(_i64p), a_bl.ctypes.data_as(_i64p), int(max_item_blocks),
-            ctypes.byref(info))
-    _check(_lib.lazy_attn_plan_shared_decode(*args, None, 0), "lazy_attn_plan_shared_decode")
+            a_bs.ctypes.data_as(_i64p), a_bl.ctypes.data_as(_i64p))
+    _check(_lib.lazy_attn_plan_shared_decode(*args, int(max_item_blocks), ctypes.byref(info),
+                                             None, 0), "lazy_attn_plan_shared_decode")
     blob = np.zeros(int(info.plan_bytes), np.uint8)
-    _check(_lib.lazy_attn_plan_shared_decode(*args, blob.ctypes.data, blob.nbytes),
+    _check(_lib.lazy_attn_plan_shared_decode(*args, int(info.max_item_blocks), ctypes.byref(info),
+                                             blob.ctypes.data, blob.nbytes),
            "lazy_attn_plan_shared_decode")
     return info, blob
 

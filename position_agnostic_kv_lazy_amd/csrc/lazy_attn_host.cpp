@@ -248,6 +248,12 @@ double shared_decode_time_us(const std::vector<int64_t>& unit_blocks,
   constexpr double kBlockBytes = 2.0 * 16 * 128 * 2;   // K and V of one block, one kv head
   constexpr double kPartialBytes = (128 + 2) * 4 * 2;  // one partial row written and read
   constexpr double kCombineUs = 2.0;
+  // Every task comes in Hkv identical copies (one per kv head), so the
+  // longest-first schedule on `slots` slots is Hkv-fold symmetric: it is the
+  // schedule of one copy per task on slots / Hkv slots, with Hkv times as many
+  // waves streaming.
+  const int64_t copies = (slots >= Hkv && slots % Hkv == 0) ? Hkv : 1;
+  const int64_t sim_slots = slots / copies;
   std::vector<double> work;
   int64_t partials = 0;
   for (size_t u = 0; u < unit_blocks.size(); ++u) {
@@ -257,7 +263,7 @@ double shared_decode_time_us(const std::vector<int64_t>& unit_blocks,
     for (int64_t k = 0; k < ch.n; ++k) {
       const double w = kPrologueSteps + static_cast<double>(ch.begin(k + 1) - ch.begin(k));
       for (int64_t m0 = 0; m0 < nm; m0 += C)
-        for (int h = 0; h < Hkv; ++h) work.push_back(w);
+        for (int64_t h = 0; h < Hkv / copies; ++h) work.push_back(w);
     }
   }
   std::sort(work.begin(), work.end(), std::greater<double>());
@@ -266,12 +272,12 @@ double shared_decode_time_us(const std::vector<int64_t>& unit_blocks,
   std::priority_queue<double, std::vector<double>, std::greater<double>> finish;
   size_t next = 0;
   double x = 0.0, t = 0.0;
-  for (; next < work.size() && static_cast<int64_t>(finish.size()) < slots; ++next)
+  for (; next < work.size() && static_cast<int64_t>(finish.size()) < sim_slots; ++next)
     finish.push(work[next]);
   while (!finish.empty()) {
     const double xf = finish.top();
-    const double step =
-        std::max(kStepLatencyUs, static_cast<double>(finish.size()) * kBlockBytes / kBytesPerUs);
+    const double waves = static_cast<double>(finish.size() * copies);
+    const double step = std::max(kStepLatencyUs, waves * kBlockBytes / kBytesPerUs);
     t += (xf - x) * step;
     x = xf;
     finish.pop();

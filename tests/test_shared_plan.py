@@ -117,6 +117,27 @@ def test_automatic_chunk_length():
         assert items[:, 1].max() <= info.max_item_blocks
 
 
+def test_passing_the_chosen_length_back_gives_the_same_plan():
+    import ctypes
+    from position_agnostic_kv_lazy_amd import binding as B
+    w = make_config(2, scale_down=2)
+    p = _params(num_blocks=w.num_blocks, max_pos=w.table_rows())
+    a = B._segment_arrays(w.requests)
+    ptrs = (a[0].ctypes.data_as(B._i64p), a[1].ctypes.data_as(B._i64p),
+            a[2].ctypes.data_as(B._i64p), a[3].ctypes.data_as(B._u8p),
+            a[4].ctypes.data_as(B._i64p), a[5].ctypes.data_as(B._i64p))
+    info = B.la_shared_plan_info()
+    assert B._lib.lazy_attn_plan_shared_decode(ctypes.byref(p), len(w.requests), *ptrs, 0,
+                                               ctypes.byref(info), None, 0) == 0
+    auto = np.zeros(int(info.plan_bytes), np.uint8)
+    assert B._lib.lazy_attn_plan_shared_decode(ctypes.byref(p), len(w.requests), *ptrs, 0,
+                                               ctypes.byref(info), auto.ctypes.data,
+                                               auto.nbytes) == 0
+    info2, fixed = la.lazy_attn_plan_shared_decode(p, w.requests, int(info.max_item_blocks))
+    assert info2.max_item_blocks == info.max_item_blocks
+    assert np.array_equal(auto, fixed)
+
+
 def test_chunks_of_a_unit_differ_by_at_most_one_block():
     doc = np.arange(10)  # 10 blocks, shared by two requests
     reqs = [[Segment(0, 160, doc, False)], [Segment(500, 160, doc, False)]]
