@@ -85,6 +85,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -290,7 +291,6 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sacc[i] - mnew);
-    lrun = lrun * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
     mrun = mnew;
 #pragma unroll
     for (int j = 0; j < 8; ++j) oacc[j] *= alpha;
@@ -298,6 +298,13 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
     uint2 pb;
     pb.x = pack_bf16x2(p[0], p[1]);
     pb.y = pack_bf16x2(p[2], p[3]);
+    // l sums the same bf16-rounded weights that multiply V, so every output
+    // row is an exact convex combination of the V rows for those weights
+    lrun = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pb.x),
+                                           __builtin_bit_cast(bf16x2v, 0x3F803F80u),
+                                           lrun * alpha, false);
+    lrun = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pb.y),
+                                           __builtin_bit_cast(bf16x2v, 0x3F803F80u), lrun, false);
     if (w.n_valid < BS) {
       // Unused slots may hold anything (even NaN): zero their V entries.
       const int k0 = 4 * gq;

@@ -54,6 +54,7 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -408,10 +409,17 @@ __global__ __launch_bounds__(256, 2) void decode_shared_kernel(
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sacc[i] - mrun[ct]);
-      lrun[ct] += (p[0] + p[1]) + (p[2] + p[3]);
       uint2 pb;
       pb.x = pack_bf16x2(p[0], p[1]);
       pb.y = pack_bf16x2(p[2], p[3]);
+      // l sums the same bf16-rounded weights that multiply V, so every output
+      // row is an exact convex combination of the V rows for those weights
+      lrun[ct] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pb.x),
+                                                 __builtin_bit_cast(bf16x2v, 0x3F803F80u),
+                                                 lrun[ct], false);
+      lrun[ct] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pb.y),
+                                                 __builtin_bit_cast(bf16x2v, 0x3F803F80u),
+                                                 lrun[ct], false);
       const i16x4 pbv = as_i16x4(pb);
 #pragma unroll
       for (int j = 0; j < 8; ++j)

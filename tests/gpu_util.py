@@ -67,14 +67,14 @@ class Device:
 
     def run(self, w, split_blocks=0, target_workgroups=0, validate=True, max_pos=None,
             pool_mode="position_free", pos_encoding="rope_half", table=None, shared=False,
-            max_item_blocks=0):
+            max_item_blocks=0, check_tables=False):
         import torch
         from position_agnostic_kv_lazy_amd import lazy_attn_validate_table
         from position_agnostic_kv_lazy_amd.prepare import prepare
         db = prepare(w, self.k, self.v, split_blocks=split_blocks,
                      target_workgroups=target_workgroups, max_pos=max_pos, pool_mode=pool_mode,
                      pos_encoding=pos_encoding, table=table, shared=shared,
-                     max_item_blocks=max_item_blocks)
+                     max_item_blocks=max_item_blocks, check_tables=check_tables)
         if validate:
             cu = None if w.kind == "decode" else np.asarray(w.cu_q, np.int32)
             lazy_attn_validate_table(db.params, db.batch, db.host_words, db.host_rbs,

@@ -80,9 +80,72 @@ def test_random_case(i):
         for r in range(w.batch):
             assert_parity(out[r], ref[r][0], w.dtype, f"case {i} req {r}")
             assert_lse(lse[r], ref[r][1], w.dtype, f"case {i} req {r}")
+        if w.dtype == "bf16" and enc != "alibi":  # the shared-segment decode too
+            mib = [0, 1, 3][i % 3]
+            out, lse, _ = dev.run(w, pool_mode=pool, pos_encoding=enc, shared=True,
+                                  max_item_blocks=mib, check_tables=True)
+            for r in range(w.batch):
+                assert_parity(out[r], ref[r][0], w.dtype, f"case {i} shared req {r}")
+                assert_lse(lse[r], ref[r][1], w.dtype, f"case {i} shared req {r}")
     else:
         ref = run_prefill(w, **kw)
         for r in range(w.batch):
             a, b = int(w.cu_q[r]), int(w.cu_q[r + 1])
             assert_parity(out[a:b], ref[r][0], w.dtype, f"case {i} req {r}")
             assert_lse(lse[a:b], ref[r][1], w.dtype, f"case {i} req {r}")
+
+
+N_SHARED = 20
+
+
+def _shared_case(i):
+    """A decode batch with heavy sharing: up to 12 requests drawing from a few
+    documents (Zipf-like), repeats within a request, explicit offsets, private
+    segments; every group size and both pool modes; chunk lengths forced down
+    to one block."""
+    rng = np.random.default_rng([7300, i])
+    Hq, Hkv = GROUPS[i % len(GROUPS)]
+    enc = ["rope_half", "rope_interleaved"][int(rng.integers(2))]
+    pool = ["position_free", "doc_local"][int(rng.integers(2))]
+    n_docs = int(rng.integers(2, 6))
+    doc_lens = [int(x) for x in rng.integers(1, 101, size=n_docs)]
+    pop = 1.0 / np.arange(1, n_docs + 1)
+    pop /= pop.sum()
+    requests = []
+    for _ in range(int(rng.integers(1, 13))):
+        items = []
+        for _ in range(int(rng.integers(1, 6))):
+            d = int(rng.choice(n_docs, p=pop))
+            if rng.random() < 0.4:
+                items.append(("doc", d, int(rng.integers(0, 600))))
+            else:
+                items.append(("doc", d))
+        if rng.random() < 0.6:
+            items.append(("priv", int(rng.integers(1, 40))))
+        requests.append(items)
+    mib = [0, 1, 2, 5, 16][int(rng.integers(5))]
+    w = build_workload(name=f"shared{i}", kind="decode", dtype="bf16", num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=128, block_size=16, rope_base=5e5,
+                       doc_lens=doc_lens, requests=requests, seed=7400 + i)
+    return w, enc, pool, mib
+
+
+@pytest.mark.parametrize("i", range(N_SHARED))
+def test_random_shared_case(i):
+    w, enc, pool, mib = _shared_case(i)
+    log(f"random shared case {i}: Hq={w.num_q_heads} Hkv={w.num_kv_heads} {enc} {pool} "
+        f"chunk={mib} batch={w.batch}")
+    if enc == "rope_interleaved" or pool == "doc_local":
+        k, v, slots, idx = segment_writes(w, "index")
+        kd, vd = store_pool(w, k, v, slots, idx if pool == "doc_local" else None,
+                            pos_encoding=enc)
+        torch.cuda.synchronize()
+        dev = Device.from_device_pools(kd, vd)
+    else:
+        dev = Device(w)
+    out, lse, _ = dev.run(w, pool_mode=pool, pos_encoding=enc, shared=True, max_item_blocks=mib,
+                          check_tables=True)
+    ref = run_decode(w, pairing="interleaved" if enc == "rope_interleaved" else "half")
+    for r in range(w.batch):
+        assert_parity(out[r], ref[r][0], "bf16", f"shared case {i} req {r}")
+        assert_lse(lse[r], ref[r][1], "bf16", f"shared case {i} req {r}")
