@@ -95,7 +95,7 @@ def test_random_case(i):
             assert_lse(lse[a:b], ref[r][1], w.dtype, f"case {i} req {r}")
 
 
-N_SHARED = 20
+N_SHARED = 48
 
 
 def _shared_case(i):
