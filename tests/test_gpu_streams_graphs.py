@@ -2,7 +2,7 @@
 
 * Decode and prefill captured into one HIP graph (torch.cuda.CUDAGraph on a
   side stream) replay to the eager result, replay after replay, with eager
-  work and synchronisations between replays.
+  work and synchronisations between replays; the shared-segment decode too.
 * Calls from two host threads on two streams, interleaved, give the results
   of the same calls made alone.
 """
@@ -56,6 +56,33 @@ def test_graph_replays_match_eager():
         log(f"graph replay {rep}")
         np.testing.assert_array_equal(dd.out_f32(), eager_d)
         np.testing.assert_array_equal(dp.out_f32(), eager_p)
+        del scratch
+
+
+def test_shared_decode_graph_replays_match_eager():
+    """The shared-segment decode (decode + merge kernels) captured alone."""
+    dec, _ = _pair()
+    kd, vd = upload_pool(dec.k_pool, dec.v_pool)
+    ds = prepare(dec, kd, vd, shared=True)
+    ds.run()
+    torch.cuda.synchronize()
+    eager = ds.out_f32().copy()
+    eager_lse = ds.lse.cpu().numpy().copy()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        ds.run(side)
+    for rep in range(4):
+        ds.out.zero_()
+        ds.lse.zero_()
+        ds.workspace.zero_()  # partials are rewritten by every replay
+        scratch = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"shared graph replay {rep}")
+        np.testing.assert_array_equal(ds.out_f32(), eager)
+        np.testing.assert_array_equal(ds.lse.cpu().numpy(), eager_lse)
         del scratch
 
 
