@@ -442,6 +442,10 @@ LA_API la_status lazy_attn_decode_noalloc(const la_params* p, const void* q, con
  *                    across steps, pays for the search once)
  *   plan             host out, info->plan_bytes bytes; NULL = sizes only
  *   plan_capacity    bytes available at plan
+ * seg_is_new is accepted for symmetry with lazy_attn_pack_segments and not
+ * read: a decode query attends every listed key, so no block is causal (in a
+ * LA_POOL_DOC_LOCAL pool a new-token segment is read like any other segment,
+ * its keys indexed from its own start).
  * bf16 only (LA_ERR_UNSUPPORTED for LA_FP32 and LA_ALIBI); the same checks
  * as lazy_attn_pack_segments.
  */
