@@ -1,6 +1,6 @@
 """Seeded random sweep of small cases across every kernel variant, against the oracle.
 
-Each case draws its own document lengths (1..100 tokens, so ragged tails and
+Each small case draws its own document lengths (1..100 tokens, so ragged tails and
 one-token blocks occur), request mixes (documents shared between and within
 requests, explicit offsets leaving gaps, keys after the decode query),
 GQA group, dtype, pool mode (position-free or document-local), positional
@@ -149,3 +149,82 @@ def test_random_shared_case(i):
     for r in range(w.batch):
         assert_parity(out[r], ref[r][0], "bf16", f"shared case {i} req {r}")
         assert_lse(lse[r], ref[r][1], "bf16", f"shared case {i} req {r}")
+
+
+N_MEDIUM = 16
+MEDIUM_GROUPS = GROUPS + [(32, 8)]
+
+
+def _medium_case(i):
+    """Longer documents (100..2000 tokens): several split groups and chunks per
+    request in decode (both kernels), multi-tile causal prefill (up to 600 new
+    tokens, many q tiles), every encoding and both pool modes."""
+    rng = np.random.default_rng([7500, i])
+    kind = "decode" if i % 2 == 0 else "prefill"
+    dtype = "f32" if i % 4 == 3 else "bf16"
+    Hq, Hkv = MEDIUM_GROUPS[int(rng.integers(len(MEDIUM_GROUPS)))]
+    enc = ["rope_half", "rope_interleaved", "alibi"][int(rng.integers(3))]
+    pool = "position_free" if enc == "alibi" else ["position_free", "doc_local"][int(rng.integers(2))]
+    n_docs = int(rng.integers(3, 7))
+    doc_lens = [int(x) for x in rng.integers(100, 2001, size=n_docs)]
+    requests = []
+    for _ in range(int(rng.integers(1, 6))):
+        items = []
+        for _ in range(int(rng.integers(2, 6))):
+            d = int(rng.integers(n_docs))
+            if kind == "decode" and rng.random() < 0.3:
+                items.append(("doc", d, int(rng.integers(0, 20000))))
+            else:
+                items.append(("doc", d))
+        if kind == "decode":
+            if rng.random() < 0.5:
+                items.append(("priv", int(rng.integers(1, 300))))
+        else:
+            items.append(("new", int(rng.integers(64, 601))))
+        requests.append(items)
+    w = build_workload(name=f"medium{i}", kind=kind, dtype=dtype, num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=128, block_size=16, rope_base=5e5,
+                       doc_lens=doc_lens, requests=requests, seed=7600 + i)
+    return w, enc, pool, rng
+
+
+@pytest.mark.parametrize("i", range(N_MEDIUM))
+def test_random_medium_case(i):
+    w, enc, pool, rng = _medium_case(i)
+    log(f"random medium case {i}: {w.kind} {w.dtype} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+        f"{enc} {pool} batch={w.batch} keys={[sum(s.n_tokens for s in r) for r in w.requests]}")
+    if enc == "rope_interleaved" or pool == "doc_local":
+        k, v, slots, idx = segment_writes(w, "index")
+        kd, vd = store_pool(w, k, v, slots, idx if pool == "doc_local" else None,
+                            pos_encoding=enc)
+        torch.cuda.synchronize()
+        dev = Device.from_device_pools(kd, vd)
+    else:
+        dev = Device(w)
+    out, lse, _ = dev.run(w, pool_mode=pool, pos_encoding=enc)
+    kw = dict(pairing="interleaved" if enc == "rope_interleaved" else "half",
+              alibi=alibi_slopes(w.num_q_heads) if enc == "alibi" else None)
+    if w.kind == "decode":
+        ref = run_decode(w, **kw)
+        for r in range(w.batch):
+            assert_parity(out[r], ref[r][0], w.dtype, f"medium {i} req {r}")
+            assert_lse(lse[r], ref[r][1], w.dtype, f"medium {i} req {r}")
+        if w.dtype == "bf16" and enc != "alibi":
+            out, lse, _ = dev.run(w, pool_mode=pool, pos_encoding=enc, shared=True,
+                                  check_tables=True)
+            for r in range(w.batch):
+                assert_parity(out[r], ref[r][0], w.dtype, f"medium {i} shared req {r}")
+                assert_lse(lse[r], ref[r][1], w.dtype, f"medium {i} shared req {r}")
+    else:
+        # rows sampled per request (the first and last included): the oracle
+        # computes each sampled row over the request's whole key list
+        rows = {}
+        for r in range(w.batch):
+            nq = w.q_len(r)
+            pick = rng.choice(nq, size=min(nq, 24), replace=False)
+            rows[r] = np.unique(np.concatenate([pick, [0, nq - 1]]))
+        ref = run_prefill(w, rows=rows, **kw)
+        for r, rr in rows.items():
+            a = int(w.cu_q[r])
+            assert_parity(out[a + rr], ref[r][0], w.dtype, f"medium {i} req {r}")
+            assert_lse(lse[a + rr], ref[r][1], w.dtype, f"medium {i} req {r}")
